@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs for attention forward and backward.
+
+This module holds no attention arithmetic: it only draws random tensors.  The
+GPU path, the oracle, the tests and the benchmark all take their inputs from
+here, so both sides see bit-identical values.
+
+The five workloads are the shapes named for this method: a tiny and a small
+causal fp32 case, the fp32 shape whose N x N score tensor is the 67 MB the
+article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype Paved
+the Way for High-Performance WebGPU Flash Attention 2" (section "Memory
+Bandwidth Optimization") says is no longer moved per layer and step, the
+large bf16 causal case, and a ragged non-causal bf16 stress case whose Q and K
+are scaled by 8 so the online-softmax maximum is rescaled often.
+
+Recipe (identical for every workload): a CPU ``torch.Generator`` seeded with
+the workload's seed draws ``torch.randn`` tensors of shape [B, H, N, d] in
+float32, in the order q, k, v, dO.  Where ``qk_mult`` is not 1 (a power of two,
+so exact), q and k are multiplied by it.  bf16 workloads then round every
+tensor to bfloat16 (round to nearest even).  The oracle receives the same
+tensors converted to float64, so input rounding is never counted as error.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    seed: int
+    qk_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def describe(self) -> str:
+        return "%s B%d H%d N%d d%d %s %s" % (
+            self.name, self.B, self.H, self.N, self.d, self.dtype,
+            "causal" if self.causal else "non-causal")
+
+
+WORKLOADS = {
+    1: Workload("tiny_causal_f32", 1, 2, 64, 16, "f32", True, 1),
+    2: Workload("small_causal_f32", 4, 4, 256, 32, "f32", True, 2),
+    3: Workload("mega_class_causal_f32", 8, 8, 512, 64, "f32", True, 3),
+    4: Workload("large_causal_bf16", 4, 16, 4096, 128, "bf16", True, 4),
+    5: Workload("ragged_noncausal_bf16", 16, 12, 1000, 64, "bf16", False, 5, 8.0),
+}
+
+
+def make_inputs(w: Workload, seed: int | None = None, device: str | torch.device = "cpu"):
+    """Return (q, k, v, dO) for workload ``w`` on ``device`` in its dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else int(seed))
+    shp = w.shape()
+    q = torch.randn(shp, generator=g, dtype=torch.float32)
+    k = torch.randn(shp, generator=g, dtype=torch.float32)
+    v = torch.randn(shp, generator=g, dtype=torch.float32)
+    dO = torch.randn(shp, generator=g, dtype=torch.float32)
+    if w.qk_mult != 1.0:
+        q = q * w.qk_mult
+        k = k * w.qk_mult
+    out = []
+    for t in (q, k, v, dO):
+        t = t.to(w.torch_dtype).contiguous()
+        if str(device) != "cpu":
+            t = t.to(device)
+        out.append(t)
+    return tuple(out)
+
+
+def custom(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
+           qk_mult: float = 1.0, name: str = "custom") -> Workload:
+    """A workload outside the named five (edge-case shapes in the tests)."""
+    return Workload(name, B, H, N, d, dtype, causal, seed, qk_mult)

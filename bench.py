@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""FlashAttention-2 forward + backward throughput on one MI355X.
+
+One step = the whole hot path over one batch of the large causal bf16
+workload (B=4, H=16, N=4096, d=128): ``fa2_forward`` and then the three
+backward stages (D preprocessing, the key-tile kernel, dQ conversion),
+i.e. exactly ``fa2_backward``, called stage by stage so that HIP events on
+the launch stream can time each kernel.  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
+
+Counted FLOP (causal halves it): forward 4*B*H*N^2*d/2, backward 2.5x that
+(five products, the recomputation of S counted once), step 3.5x.
+
+Prints ONE JSON line with the throughput, the roofline of the dominant
+kernel (its counted FLOP per launch over its mean event-timed duration,
+against the bf16 dense MFMA peak) and the oracle's CPU throughput on a
+bounded sample of heads of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1..5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Public MI355X figures (dense, no sparsity), TFLOP/s.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+HBM_GBS = 8000.0
+METRIC = "attention fwd+bwd TFLOP/s and % MFMA peak (bf16 B4 H16 N4096 d128 causal)"
+CSRC = os.path.join(ROOT, "tiled_attention_fwd_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def counted_flop(w):
+    fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return fwd, 2.5 * fwd, 3.5 * fwd
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources; ties stored counter readings to a kernel version."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != source_hash():
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
+    """Time the fp64 oracle (test infrastructure) on whole heads of the same
+    workload until about ``budget_s`` seconds of work are done; also report
+    the GPU's error on those heads."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.default()
+    q, k, v, dO = (t.cpu() for t in inputs)
+    o, lse, dq, dk, dv = (t.float().cpu() for t in gpu_outs)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_total = 0, 0.0
+    errs = {n: 0.0 for n in ("O", "LSE", "dQ", "dK", "dV")}
+
+    def rel(a, r):
+        a = np.asarray(a, dtype=np.float64)
+        return float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-300))
+
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        o_r, lse_r = orc.fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
+        dq_r, dk_r, dv_r = orc.bwd(q[sl], k[sl], v[sl], dO[sl], w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        for name, a, r in (("O", o[sl], o_r), ("LSE", lse[sl], lse_r), ("dQ", dq[sl], dq_r),
+                           ("dK", dk[sl], dk_r), ("dV", dv[sl], dv_r)):
+            errs[name] = max(errs[name], rel(a, r))
+        if t_total >= budget_s:
+            break
+    step_flop_per_head = counted_flop(w)[2] / (w.B * w.H)
+    value = step_flop_per_head * done / t_total / 1e12
+    return {
+        "value": value, "unit": "TFLOP/s", "cores": orc.max_threads(), "kind": "oracle",
+        "sample": "%d of %d heads of %s, fp64 forward+backward, %.1f s" % (done, len(heads), w.name, t_total),
+    }, {"heads_checked": done, "max_rel_err": errs}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import tiled_attention_fwd_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, dO = workloads.make_inputs(w, seed=args.seed, device=dev)
+    B, H, N, d = w.shape()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(max(fa.fa2_backward_workspace_size(B, H, N, d, q.dtype), 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.fa2_forward(q, k, v, o, lse, w.causal, w.scale, stream)
+        for s in (1, 2, 3):
+            if evs:
+                evs[s].record(stream)
+            fa.fa2_backward_stage(s, q, k, v, o, dO, lse, dq, dk, dv, w.causal, w.scale, ws, stream)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    # N = 1: there is no process group, so the barrier reduces to the sync.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    names = ["fwd_kernel", "bwd_pre_kernel", "bwd_kernel", "dq_convert_kernel"]
+    per = {n: [events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)] for i, n in enumerate(names)}
+    mean_ms = {n: statistics.fmean(x) for n, x in per.items()}
+    fwd_f, bwd_f, step_f = counted_flop(w)
+    bwd_ms = mean_ms["bwd_pre_kernel"] + mean_ms["bwd_kernel"] + mean_ms["dq_convert_kernel"]
+    peak = PEAK_TFLOPS[w.dtype]
+    value = step_f / (ms_per_step * 1e-3) / 1e12
+
+    dom = "bwd_kernel" if mean_ms["bwd_kernel"] >= mean_ms["fwd_kernel"] else "fwd_kernel"
+    dom_flop = bwd_f if dom == "bwd_kernel" else fwd_f
+    achieved = dom_flop / (mean_ms[dom] * 1e-3) / 1e12
+    traffic = stored_traffic(dom, w.name)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic,
+                "mean_launch_ms": mean_ms[dom], "flop_per_launch": dom_flop}
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "seed": w.seed if args.seed is None else args.seed},
+        "roofline": roofline,
+    }
+    detail = {
+        "fwd": {"ms": mean_ms["fwd_kernel"], "tflops": fwd_f / (mean_ms["fwd_kernel"] * 1e-3) / 1e12},
+        "bwd": {"ms": bwd_ms, "tflops": bwd_f / (bwd_ms * 1e-3) / 1e12},
+        "step_events_ms": mean_ms["fwd_kernel"] + bwd_ms,
+        "kernel_ms": mean_ms,
+        "peak_tflops": peak,
+    }
+    for kk in ("fwd", "bwd"):
+        detail[kk]["frac_peak"] = detail[kk]["tflops"] / peak
+    detail["step_frac_peak"] = value / peak
+    detail["source_hash"] = source_hash()
+    if args.cpu_budget > 0:
+        cb, parity = cpu_baseline(w, (q, k, v, dO), (o, lse, dq, dk, dv), args.cpu_budget)
+        result["cpu_baseline"] = cb
+        detail["parity_sampled_heads"] = parity
+    else:
+        result["cpu_baseline"] = None
+    result["detail"] = detail
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,117 @@
+/*
+ * fa2.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library, libfa2.so.
+ *
+ * The operation is scaled dot-product attention computed blockwise, as the
+ * article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype
+ * Paved the Way for High-Performance WebGPU Flash Attention 2" describes in
+ * its section "Translating to WGSL and Optimizing Passes": the forward pass
+ * walks K and V block by block with the online-softmax state held in
+ * registers and never writes the N x N attention matrix to global memory;
+ * the backward pass rebuilds the attention weights from Q, K and the saved
+ * log-sum-exp instead of reading a cached matrix.
+ *
+ * Definitions (per batch b and head h; i, j index rows of the sequence):
+ *   S_ij  = scale * q_i . k_j, with S_ij = -inf for j > i when causal
+ *   LSE_i = ln sum_j exp(S_ij)          (natural log, scaled masked logits)
+ *   P_ij  = exp(S_ij - LSE_i)
+ *   O_i   = sum_j P_ij v_j
+ *   dQ, dK, dV = gradients of L = sum(O * dO) for the upstream gradient dO.
+ *
+ * Layout and ownership (every call):
+ *   - q, k, v, o, dO, dq, dk, dv are DEVICE pointers to contiguous row-major
+ *     [B, H, N, d] arrays of the element type `dtype` (FA2_F32: float,
+ *     FA2_BF16: bfloat16).  lse is a device float array [B, H, N].
+ *   - Every pointer must be 16-byte aligned.  Outputs must not alias inputs
+ *     or each other.
+ *   - The caller owns every buffer (inputs, outputs, workspace).  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; results are valid once the stream
+ *     has completed it.  Calls are reentrant and thread-safe.
+ *
+ * Errors: every call returns an fa2_status and never aborts.  Arguments are
+ * validated before any HIP call is made, so a rejected call touches no
+ * device state.  B, H or N equal to 0 is a valid empty problem: FA2_OK and
+ * nothing is launched.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA2_F32 = 0, FA2_BF16 = 1 } fa2_dtype;
+
+typedef enum {
+  FA2_OK = 0,
+  FA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, scale not finite
+                              or not > 0, dtype not an fa2_dtype, size
+                              overflow (N * d must stay below 2^31)        */
+  FA2_ERR_UNSUPPORTED = 2, /* d not in {16, 32, 64, 128}, or a pointer not
+                              16-byte aligned                              */
+  FA2_ERR_WORKSPACE = 3,   /* backward workspace NULL or too small         */
+  FA2_ERR_LAUNCH = 4       /* a HIP launch reported an error               */
+} fa2_status;
+
+/*
+ * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float, natural
+ * log).  Arithmetic: the two products run on MFMA with fp32 accumulation
+ * (bf16 operands for FA2_BF16, fp32 operands for FA2_F32); the softmax
+ * state is fp32; in bf16 mode the weights P are rounded to bf16 (nearest
+ * even) before the second product and o is rounded to nearest even.
+ * scale: the factor on q . k (commonly 1/sqrt(d)); must be finite and > 0.
+ * causal: nonzero keeps keys j <= i (top-left aligned).
+ */
+int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal, int dtype,
+                void* stream);
+
+/*
+ * Bytes of device workspace fa2_backward needs for this problem (0 for an
+ * empty one).  The workspace holds D = rowsum(dO * O) as float [B,H,N] and,
+ * in bf16 mode, an fp32 dQ accumulator [B,H,N,d]; its contents on entry do
+ * not matter and on return are unspecified.  Returns 0 for invalid sizes.
+ */
+size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass for the loss L = sum(O * dO).  o and lse must be the outputs
+ * of fa2_forward for the same q, k, v, scale and causal.  Overwrites dq, dk,
+ * dv (never accumulates into them).  Kernels, in stream order:
+ *   1. D_i = sum_k dO_ik O_ik (fp32) and zeroing of the dQ accumulator;
+ *   2. a key-tile-parallel kernel that recomputes P from q, k and lse,
+ *      accumulates dK and dV in registers and adds dQ partial sums into the
+ *      fp32 accumulator with atomics (their order varies, so dq may differ
+ *      between runs in the last bits);
+ *   3. in bf16 mode, conversion of the dQ accumulator to bf16.
+ * workspace / workspace_bytes: device buffer of at least
+ * fa2_backward_workspace_size(B, H, N, d, dtype) bytes, 16-byte aligned.
+ */
+int fa2_backward(const void* q, const void* k, const void* v, const void* o,
+                 const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, float scale, int causal, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One stage of fa2_backward, with exactly fa2_backward's arguments and
+ * checks: stage 1 = D and accumulator zeroing, 2 = the key-tile kernel,
+ * 3 = dQ conversion (a no-op in fp32 mode).  Enqueuing stages 1, 2, 3 in
+ * order on one stream is fa2_backward; the split lets a caller record
+ * events around the key-tile kernel.  Any other stage: FA2_ERR_INVALID_ARG.
+ */
+int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                       const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int H, int N, int d, float scale, int causal, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -53,7 +53,12 @@ class Oracle:
         lib.oracle_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, L,
                                        ctypes.c_double, ctypes.c_int]
         lib.oracle_bwd_f64.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
 
     def fwd(self, q, k, v, scale: float, causal: bool):
         """Return (O, LSE) in fp64 for [B, H, N, d] inputs (numpy or CPU torch)."""

@@ -47,8 +47,12 @@
  * allocation fails.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads an OpenMP region of this library will use (reported with timings). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 static int bad_args(long B, long H, long N, long d) {
   return B < 0 || H < 0 || N < 0 || d <= 0;

@@ -1,0 +1,133 @@
+"""The C ABI of libfa2.so on the CPU: it loads, exports every declared entry
+point, and rejects bad arguments with the documented status codes before any
+HIP call (so no GPU is needed).  Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_attention_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+A = 0x10000  # a fake, 16-byte aligned, never dereferenced address
+MIS = 0x10008  # a fake misaligned address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        from tiled_attention_fwd_amd import build
+        build.build()
+    return fa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names == ["fa2_backward", "fa2_backward_stage", "fa2_backward_workspace_size", "fa2_forward",
+                     "fa2_status_string"]
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def fwd(L, q=A, k=A, v=A, o=A, lse=A, B=1, H=2, N=64, d=64, scale=0.125, causal=1, dtype=1):
+    return L.fa2_forward(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def bwd(L, ptr=A, B=1, H=2, N=64, d=64, scale=0.125, causal=1, dtype=1, ws=A, wsb=None, **over):
+    p = dict(q=ptr, k=ptr, v=ptr, o=ptr, dO=ptr, lse=ptr, dq=ptr, dk=ptr, dv=ptr)
+    p.update(over)
+    if wsb is None:
+        wsb = L.fa2_backward_workspace_size(B, H, N, d, dtype)
+    return L.fa2_backward(p["q"], p["k"], p["v"], p["o"], p["dO"], p["lse"], p["dq"], p["dk"], p["dv"],
+                          B, H, N, d, scale, causal, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o", "lse"])
+def test_forward_null_pointer(L, arg):
+    assert fwd(L, **{arg: None}) == fa.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), fa.FA2_ERR_INVALID_ARG), (dict(H=-2), fa.FA2_ERR_INVALID_ARG),
+    (dict(N=-3), fa.FA2_ERR_INVALID_ARG), (dict(d=0), fa.FA2_ERR_INVALID_ARG),
+    (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(d=256), fa.FA2_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA2_ERR_INVALID_ARG), (dict(dtype=-1), fa.FA2_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA2_ERR_INVALID_ARG), (dict(scale=-0.5), fa.FA2_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA2_ERR_INVALID_ARG), (dict(scale=float("inf")), fa.FA2_ERR_INVALID_ARG),
+    (dict(q=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(lse=MIS), fa.FA2_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, d=128), fa.FA2_ERR_INVALID_ARG),
+])
+def test_forward_rejects(L, kw, status):
+    assert fwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_empty_problem_is_noop(L, kw):
+    # null data pointers are fine for an empty problem: nothing is launched
+    assert fwd(L, q=None, k=None, v=None, o=None, lse=None, **kw) == fa.FA2_OK
+    assert bwd(L, ptr=None, ws=None, wsb=0, **kw) == fa.FA2_OK
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o", "dO", "lse", "dq", "dk", "dv"])
+def test_backward_null_and_misaligned(L, arg):
+    assert bwd(L, **{arg: None}) == fa.FA2_ERR_INVALID_ARG
+    assert bwd(L, **{arg: MIS}) == fa.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_backward_workspace_checks(L, dtype):
+    need = L.fa2_backward_workspace_size(1, 2, 64, 64, dtype)
+    assert need > 0
+    assert bwd(L, dtype=dtype, ws=None, wsb=need) == fa.FA2_ERR_WORKSPACE
+    assert bwd(L, dtype=dtype, wsb=need - 1) == fa.FA2_ERR_WORKSPACE
+    assert bwd(L, dtype=dtype, ws=MIS, wsb=need) == fa.FA2_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula(L):
+    def al(x):
+        return (x + 255) // 256 * 256
+    B, H, N, d = 4, 16, 4096, 128
+    rows = B * H * N
+    assert L.fa2_backward_workspace_size(B, H, N, d, 1) == al(rows * 4) + al(rows * d * 4)
+    assert L.fa2_backward_workspace_size(B, H, N, d, 0) == al(rows * 4)
+    assert L.fa2_backward_workspace_size(0, H, N, d, 1) == 0
+    assert L.fa2_backward_workspace_size(B, H, N, 40, 1) == 0
+    assert L.fa2_backward_workspace_size(-1, H, N, d, 1) == 0
+
+
+def test_status_strings(L):
+    for s in range(5):
+        txt = L.fa2_status_string(s).decode()
+        assert txt.startswith("FA2_")
+    assert b"unknown" in L.fa2_status_string(99)
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
+
+
+@pytest.mark.parametrize("stage", [0, 4, -1])
+def test_backward_stage_rejects_bad_stage(L, stage):
+    n = L.fa2_backward_workspace_size(1, 2, 64, 64, 1)
+    assert L.fa2_backward_stage(stage, A, A, A, A, A, A, A, A, A, 1, 2, 64, 64, 0.125, 1, 1, A, n, None) \
+        == fa.FA2_ERR_INVALID_ARG
+
+
+def test_backward_stage_validates_like_backward(L):
+    n = L.fa2_backward_workspace_size(1, 2, 64, 64, 1)
+    assert L.fa2_backward_stage(2, A, A, A, A, A, A, A, A, A, 1, 2, 64, 48, 0.125, 1, 1, A, n, None) \
+        == fa.FA2_ERR_UNSUPPORTED
+    assert L.fa2_backward_stage(1, A, A, A, A, A, A, A, A, A, 1, 2, 64, 64, 0.125, 1, 1, A, n - 1, None) \
+        == fa.FA2_ERR_WORKSPACE

@@ -1,0 +1,197 @@
+"""GPU parity: the HIP forward and backward against the fp64 oracle.
+
+Error measure, per tensor T in (O, LSE, dQ, dK, dV):
+    err(T) = max |T_gpu - T_oracle| / max |T_oracle|
+with limits 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs with fp32
+accumulation.  The oracle runs on the GPU's exact input values (bf16 inputs
+are converted to float64), so input rounding is not counted.  The GPU
+backward consumes the GPU forward's own O and LSE.
+
+Every output buffer is filled with NaN before the call (an element the
+kernels fail to write shows up as NaN), and sits inside a larger allocation
+whose guard bands are checked afterwards (an out-of-bounds write at a ragged
+tail changes them).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_fwd_amd as fa
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+GUARD = 4096  # elements of guard band on each side of every output
+CANARY = -12288.0  # exactly representable in bf16 and fp32
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not np.all(np.isfinite(gpu)):
+        return float("inf")
+    denom = float(np.max(np.abs(ref)))
+    diff = float(np.max(np.abs(gpu - ref)))
+    return diff / denom if denom > 0 else diff
+
+
+class Guarded:
+    """An output tensor carved out of a bigger buffer with canary bands."""
+
+    def __init__(self, shape, dtype, device="cuda"):
+        n = int(np.prod(shape))
+        self.buf = torch.full((n + 2 * GUARD,), CANARY, dtype=dtype, device=device)
+        self.buf[GUARD:GUARD + n] = float("nan")
+        self.t = self.buf[GUARD:GUARD + n].view(shape)
+
+    def guards_intact(self):
+        lo = self.buf[:GUARD].float().cpu()
+        hi = self.buf[-GUARD:].float().cpu()
+        return bool(torch.all(lo == CANARY)) and bool(torch.all(hi == CANARY))
+
+
+def gpu_fwd_bwd(q, k, v, dO, causal, scale):
+    B, H, N, d = q.shape
+    o = Guarded(q.shape, q.dtype)
+    lse = Guarded((B, H, N), torch.float32)
+    fa.fa2_forward(q, k, v, o.t, lse.t, causal, scale)
+    dq, dk, dv = (Guarded(q.shape, q.dtype) for _ in range(3))
+    fa.fa2_backward(q, k, v, o.t, dO, lse.t, dq.t, dk.t, dv.t, causal, scale)
+    torch.cuda.synchronize()
+    for g, name in ((o, "O"), (lse, "LSE"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):
+        assert g.guards_intact(), "%s: write outside the output tensor" % name
+    return o.t, lse.t, dq.t, dk.t, dv.t
+
+
+def check_against_oracle(w, q, k, v, dO, outs, heads=None):
+    """Compare GPU outputs with the oracle, on all heads or on (b, h) pairs."""
+    o, lse, dq, dk, dv = (t.float().cpu() for t in outs)
+    qc, kc, vc, gc = (t.cpu() for t in (q, k, v, dO))
+    if heads is None:
+        sel = [(slice(None), slice(None))]
+    else:
+        sel = [(slice(b, b + 1), slice(h, h + 1)) for b, h in heads]
+    errs = {n: 0.0 for n in ("O", "LSE", "dQ", "dK", "dV")}
+    for bs, hs in sel:
+        o_r, lse_r = oracle.fwd(qc[bs, hs], kc[bs, hs], vc[bs, hs], w.scale, w.causal)
+        dq_r, dk_r, dv_r = oracle.bwd(qc[bs, hs], kc[bs, hs], vc[bs, hs], gc[bs, hs], w.scale, w.causal)
+        errs["O"] = max(errs["O"], rel_err(o[bs, hs], o_r))
+        errs["LSE"] = max(errs["LSE"], rel_err(lse[bs, hs], lse_r))
+        errs["dQ"] = max(errs["dQ"], rel_err(dq[bs, hs], dq_r))
+        errs["dK"] = max(errs["dK"], rel_err(dk[bs, hs], dk_r))
+        errs["dV"] = max(errs["dV"], rel_err(dv[bs, hs], dv_r))
+    return errs
+
+
+def run_case(w, heads=None):
+    log("case: %s seed=%d" % (w.describe(), w.seed))
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    outs = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
+    errs = check_against_oracle(w, q, k, v, dO, outs, heads)
+    log("  errors: " + " ".join("%s=%.3g" % kv for kv in errs.items()))
+    tol = TOL[w.dtype]
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, "%s exceeds tolerance %g: %r" % (w.describe(), tol, bad)
+    return errs
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_named_workload_full(wid):
+    run_case(workloads.WORKLOADS[wid])
+
+
+def test_ragged_noncausal_bf16_sampled_heads():
+    w = workloads.WORKLOADS[5]
+    run_case(w, heads=[(0, 0), (3, 7), (9, 2), (15, 11)])
+
+
+def test_large_causal_bf16_sampled_heads():
+    w = workloads.WORKLOADS[4]
+    run_case(w, heads=[(0, 0), (2, 9), (3, 15)])
+
+
+EDGE_N = [1, 2, 17, 63, 64, 65, 127, 129, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_edge_shapes(N, d, causal, dtype):
+    seed = 1000 + N * 7 + d + (1 if causal else 0) + (2 if dtype == "bf16" else 0)
+    w = workloads.custom(1, 2, N, d, dtype, causal, seed, name="edge")
+    run_case(w)
+
+
+def test_large_logits_causal_bf16():
+    """x8 Q and K (logit sigma near 64 nats) with the causal mask and a
+    ragged length: repeated max rescaling along the diagonal."""
+    run_case(workloads.custom(2, 3, 777, 128, "bf16", True, 77, qk_mult=8.0, name="stress"))
+
+
+def test_large_logits_fp32():
+    run_case(workloads.custom(1, 2, 300, 64, "f32", False, 78, qk_mult=8.0, name="stress"))
+
+
+def test_forward_bitwise_deterministic():
+    w = workloads.custom(2, 4, 1000, 128, "bf16", True, 5)
+    q, k, v, _ = workloads.make_inputs(w, device="cuda")
+    ref = None
+    for _ in range(3):
+        o, lse = fa.forward(q, k, v, True, w.scale)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (o.clone(), lse.clone())
+        else:
+            assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+
+
+def test_gpu_invariants_large_causal():
+    """Properties that hold at any size, checked on the full large workload:
+    sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per (b, h)."""
+    w = workloads.WORKLOADS[4]
+    log("case: invariants %s" % w.describe())
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
+    sk = dk.float().sum(dim=2).abs().amax() / dk.float().abs().amax()
+    sv = (dv.float().sum(dim=2) - dO.float().sum(dim=2)).abs().amax() / dO.float().sum(dim=2).abs().amax()
+    log("  sum dK rel %.3g, sum dV - sum dO rel %.3g" % (sk, sv))
+    assert sk < 2e-2 and sv < 2e-2
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_backward_repeatable_within_tolerance():
+    w = workloads.custom(1, 4, 512, 64, "bf16", True, 6)
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    o, lse = fa.forward(q, k, v, True, w.scale)
+    a = fa.backward(q, k, v, o, lse, dO, True, w.scale)
+    b = fa.backward(q, k, v, o, lse, dO, True, w.scale)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert rel_err(x.float().cpu(), y.float().cpu()) < 1e-2
+    # dK and dV come from one workgroup each, without atomics: bitwise equal
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_empty_batch_is_noop():
+    q = torch.empty((0, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.forward(q, q, q)
+    dq, dk, dv = fa.backward(q, q, q, o, lse, q)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0
+
+
+def test_rejects_bad_head_dim_on_gpu():
+    q = torch.zeros((1, 1, 16, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.Fa2Error):
+        fa.forward(q, q, q)

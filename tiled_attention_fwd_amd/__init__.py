@@ -1,0 +1,172 @@
+"""Python binding of libfa2.so, the gfx950 FlashAttention-2 library.
+
+Argument marshalling only: every step of the forward and backward passes runs
+in the HIP kernels behind the C ABI declared in ``include/fa2.h``.  PyTorch is
+used for device memory and the current stream.  There is no fallback: if the
+library is not built, importing works but every call raises ``Fa2Error``.
+
+Functions with the C names (``fa2_forward``, ``fa2_backward``,
+``fa2_backward_workspace_size``, ``fa2_status_string``) take caller-allocated
+tensors like the C ABI; ``forward`` / ``backward`` allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+FA2_F32 = 0
+FA2_BF16 = 1
+FA2_OK = 0
+FA2_ERR_INVALID_ARG = 1
+FA2_ERR_UNSUPPORTED = 2
+FA2_ERR_WORKSPACE = 3
+FA2_ERR_LAUNCH = 4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+
+_lib = None
+
+
+class Fa2Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s" % (what, fa2_status_string(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Fa2Error(FA2_ERR_LAUNCH, "libfa2.so is not built (python -m tiled_attention_fwd_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.fa2_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+        L.fa2_forward.restype = i
+        L.fa2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp,
+                                   ctypes.c_size_t, vp]
+        L.fa2_backward.restype = i
+        L.fa2_backward_stage.argtypes = [i] + L.fa2_backward.argtypes
+        L.fa2_backward_stage.restype = i
+        L.fa2_backward_workspace_size.argtypes = [i, i, i, i, i]
+        L.fa2_backward_workspace_size.restype = ctypes.c_size_t
+        L.fa2_status_string.argtypes = [i]
+        L.fa2_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def fa2_status_string(status: int) -> str:
+    try:
+        return lib().fa2_status_string(int(status)).decode()
+    except Fa2Error:
+        return "status %d" % status
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return FA2_F32
+    if t == torch.bfloat16:
+        return FA2_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t)
+
+
+def _check_tensors(ref: torch.Tensor, *ts: torch.Tensor):
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors, got %s" % (tuple(ref.shape),))
+    for t in (ref,) + ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+        if t.device != ref.device:
+            raise ValueError("tensors must be on one device")
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa2_forward(q, k, v, o, lse, causal: bool = True, scale: float | None = None, stream=None) -> None:
+    """Enqueue the forward pass into caller-allocated ``o`` and ``lse``."""
+    _check_tensors(q, k, v, o, lse)
+    B, H, N, d = q.shape
+    for t in (k, v, o):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o must share shape and dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    st = lib().fa2_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           B, H, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype),
+                           _stream(stream, q.device))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_forward")
+
+
+def fa2_backward_workspace_size(B: int, H: int, N: int, d: int, dtype) -> int:
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().fa2_backward_workspace_size(B, H, N, d, code))
+
+
+def fa2_backward(q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True, scale: float | None = None,
+                 workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue the backward pass into caller-allocated ``dq``, ``dk``, ``dv``."""
+    _backward_call(0, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def fa2_backward_stage(stage: int, q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True,
+                       scale: float | None = None, workspace: torch.Tensor | None = None,
+                       stream=None) -> None:
+    """Enqueue one backward stage (1: D, 2: key-tile kernel, 3: dQ convert)."""
+    if workspace is None:
+        raise ValueError("the stages share state through the workspace: pass one")
+    _backward_call(int(stage), q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def _backward_call(stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream):
+    _check_tensors(q, k, v, o, dO, lse, dq, dk, dv)
+    B, H, N, d = q.shape
+    for t in (k, v, o, dO, dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dO, dq, dk, dv must share shape and dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    need = fa2_backward_workspace_size(B, H, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
+            _dtype_code(q.dtype), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream(stream, q.device))
+    if stage == 0:
+        st = lib().fa2_backward(*args)
+    else:
+        st = lib().fa2_backward_stage(stage, *args)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_backward" if stage == 0 else "fa2_backward_stage(%d)" % stage)
+
+
+def forward(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
+    """Return (o, lse) for [B, H, N, d] float32 or bfloat16 GPU tensors."""
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa2_forward(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dO, causal: bool = True, scale: float | None = None,
+             workspace: torch.Tensor | None = None, stream=None):
+    """Return (dq, dk, dv) of L = sum(o * dO); o, lse come from ``forward``."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    fa2_backward(q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+    return dq, dk, dv

@@ -1,0 +1,107 @@
+// fa2_api.cpp -- the C ABI declared in include/fa2.h.
+//
+// Validation happens here, before any HIP call, so a rejected call touches
+// no device state; the launchers behind fa2_launch.hpp only ever see
+// arguments that passed these checks.
+#include "fa2.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa2_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Shared size/type checks.  Returns FA2_OK, or the status to report.
+int check_sizes(int B, int H, int N, int d, int dtype) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return FA2_ERR_INVALID_ARG;
+  if (dtype != FA2_F32 && dtype != FA2_BF16) return FA2_ERR_INVALID_ARG;
+  if (!supported_d(d)) return FA2_ERR_UNSUPPORTED;
+  // Per-head offsets are computed in int; whole-tensor offsets in size_t.
+  if ((int64_t)N * d >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;
+  if ((int64_t)B * H >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
+}
+
+bool is_empty(int B, int H, int N) { return B == 0 || H == 0 || N == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa2_status_string(int status) {
+  switch (status) {
+    case FA2_OK: return "FA2_OK";
+    case FA2_ERR_INVALID_ARG: return "FA2_ERR_INVALID_ARG: null pointer, negative size, bad scale or dtype, or size overflow";
+    case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED: head dim not in {16,32,64,128} or pointer not 16-byte aligned";
+    case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: a HIP kernel launch failed";
+    default: return "unknown fa2 status";
+  }
+}
+
+int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, int dtype, void* stream) {
+  int st = check_sizes(B, H, N, d, dtype);
+  if (st != FA2_OK) return st;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (is_empty(B, H, N)) return FA2_OK;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA2_ERR_UNSUPPORTED;
+  fa2::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, static_cast<hipStream_t>(stream)};
+  return fa2::launch_forward(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
+  if (check_sizes(B, H, N, d, dtype) != FA2_OK) return 0;
+  if (is_empty(B, H, N)) return 0;
+  return fa2::ws_total_bytes((size_t)B * H * N, d, dtype);
+}
+
+static int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v,
+                         const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, float scale, int causal, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int st = check_sizes(B, H, N, d, dtype);
+  if (st != FA2_OK) return st;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (is_empty(B, H, N)) return FA2_OK;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA2_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)B * H * N;
+  if (!workspace || workspace_bytes < fa2::ws_total_bytes(rows, d, dtype)) return FA2_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws);
+  float* dq_acc = dtype == FA2_BF16 ? reinterpret_cast<float*>(ws + fa2::ws_delta_bytes(rows))
+                                    : static_cast<float*>(dq);
+  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, delta, dq_acc,
+                 static_cast<hipStream_t>(stream)};
+  for (int s = stage_first; s <= stage_last; ++s)
+    if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;
+  return FA2_OK;
+}
+
+int fa2_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dO,
+                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                       int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
+  return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                       workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+// fa2_common.hpp -- gfx950 building blocks shared by the attention kernels.
+//
+// Everything here is about mapping tiles onto the CDNA4 32x32 MFMA:
+//   * bf16 operands use v_mfma_f32_32x32x16_bf16 (8 bf16 per lane per operand),
+//   * fp32 operands use v_mfma_f32_32x32x2_f32 (1 float per lane per operand),
+// both accumulating a 32x32 fp32 block held as 16 floats per lane.
+//
+// Lane conventions of a wave64 (l = lane, l32 = l % 32, h = l / 32):
+//   A operand  (M x K): lane supplies row  m = l32, contraction slots of half h
+//   B operand  (K x N): lane supplies column n = l32, contraction slots of half h
+//   accumulator (M x N): lane holds column n = l32 and rows
+//                        acc_row(r, h) = 8*(r/4) + 4*h + r%4 for r = 0..15.
+// A product only needs A and B to number their contraction slots the same
+// way, so every operand here is fetched as one 16-byte fragment per lane
+// ("chunk"): CH = 16 / sizeof(element) consecutive contraction elements.
+// For bf16 a chunk is one MFMA (half h covers elements 8h..8h+7 of a
+// 16-wide step); for fp32 it is four MFMAs (element e of the fragment
+// feeds step e).
+//
+// When the second product of an attention step contracts over the ROW
+// index of a previous accumulator (P or dS), the lane already holds the
+// right column and only needs its 16 accumulator values packed into chunks.
+// The matching A operand is read from an LDS tile stored transposed, with
+// the contraction index x at position swap_bits23(x) inside each group of
+// 16, which makes the rows a lane needs for one chunk contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Reinterpret whole 16-byte fragments.  (Bit-casting a single element of an
+// ext_vector, as in __builtin_bit_cast(float, v[e]), is miscompiled by the
+// ROCm 7.2 clang inside unrolled loops -- every iteration reads element 0 --
+// so elements are only ever taken from vectors of the wanted type.)
+__device__ __forceinline__ f32x4 as_f32x4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
+__device__ __forceinline__ u32x4 as_u32x4(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<float> {
+  static constexpr int CH = 4;  // elements per 16-byte fragment
+};
+template <>
+struct Elt<__bf16> {
+  static constexpr int CH = 8;
+};
+
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Position of contraction index x inside a transposed LDS tile.
+__device__ __forceinline__ int swap_bits23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// First LDS position of chunk t (accumulator registers CH*t .. CH*t+CH-1) of
+// a 32-row accumulator block, for lane half h, in a swap_bits23 tile.
+template <int CH>
+__device__ __forceinline__ int chunk_pos(int t, int h) {
+  const int r0 = CH * t;
+  return 16 * (r0 >> 3) + 8 * h + 4 * ((r0 >> 2) & 1);
+}
+
+// acc += A_fragment * B_fragment over one 16-byte chunk of the contraction.
+template <typename T>
+__device__ __forceinline__ void mfma_chunk(f32x16& acc, u32x4 a, u32x4 b);
+
+template <>
+__device__ __forceinline__ void mfma_chunk<__bf16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mfma_chunk<float>(f32x16& acc, u32x4 a, u32x4 b) {
+  const f32x4 af = as_f32x4(a), bf = as_f32x4(b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], acc, 0, 0, 0);
+}
+
+// Pack accumulator registers CH*t .. CH*t+CH-1 into one B-operand fragment
+// (bf16: round to nearest even, two per dword).
+template <typename T>
+__device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int t);
+
+template <>
+__device__ __forceinline__ u32x4 pack_chunk<__bf16>(const f32x16& x, int t) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f32x2 pr = {x[8 * t + 2 * w], x[8 * t + 2 * w + 1]};
+    r[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+  }
+  return r;
+}
+
+template <>
+__device__ __forceinline__ u32x4 pack_chunk<float>(const f32x16& x, int t) {
+  return as_u32x4(f32x4{x[4 * t], x[4 * t + 1], x[4 * t + 2], x[4 * t + 3]});
+}
+
+// Store 4 consecutive fp32 values as 4 elements of T (8 or 16 bytes).
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
+
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+}
+
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16* dst, float a, float b, float c, float d) {
+  f32x2 lo = {a, b}, hi = {c, d};
+  *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+}
+
+// A single element converted from fp32.
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) {
+  return static_cast<T>(x);
+}
+
+// Transposed write of a 4-row x CH-column block held as four 16-byte row
+// fragments: for every column x, the 4 values (rows 0..3) are written as one
+// contiguous group at dst_col(x).  `row_stride` is the LDS tile row length
+// in elements; `col0` is the first destination row of the transposed tile
+// and `pos` the destination position of row 0 (rows 1..3 follow it).
+template <typename T>
+__device__ __forceinline__ void write_transposed4(T* tile, int row_stride, int col0, int pos,
+                                                  const u32x4 (&r)[4]);
+
+template <>
+__device__ __forceinline__ void write_transposed4<float>(float* tile, int row_stride, int col0, int pos,
+                                                         const u32x4 (&r)[4]) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    *reinterpret_cast<u32x4*>(tile + (col0 + x) * row_stride + pos) = u32x4{r[0][x], r[1][x], r[2][x], r[3][x]};
+}
+
+template <>
+__device__ __forceinline__ void write_transposed4<__bf16>(__bf16* tile, int row_stride, int col0, int pos,
+                                                          const u32x4 (&r)[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // element 2w sits in the low half of dword w, element 2w+1 in the high half
+    const uint32_t lo0 = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+    const uint32_t hi0 = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+    const uint32_t lo1 = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+    const uint32_t hi1 = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+    *reinterpret_cast<u32x2*>(tile + (col0 + 2 * w) * row_stride + pos) = u32x2{lo0, hi0};
+    *reinterpret_cast<u32x2*>(tile + (col0 + 2 * w + 1) * row_stride + pos) = u32x2{lo1, hi1};
+  }
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace fa2

@@ -1,0 +1,253 @@
+// fa2_fwd.hip -- FlashAttention-2 forward pass for gfx950.
+//
+// The article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype
+// Paved the Way for High-Performance WebGPU Flash Attention 2" (section
+// "Translating to WGSL and Optimizing Passes") gives the shape of the pass:
+// one workgroup per (batch, head, query tile), keys and values visited in
+// blocks, the online-softmax state kept in registers, no N x N matrix in
+// global memory.  Section "Memory Bandwidth Optimization" adds that the
+// softmax reduction is built up block by block.  What follows is that pass
+// laid out for CDNA4.
+//
+// Workgroup: 4 waves x 32 query rows = a 128-row query tile.  Each wave
+// computes the TRANSPOSED score block S^T = K Q^T (keys x queries) on MFMA,
+// so every lane owns one query column: its running max m and sum l are
+// plain per-lane registers, the row reduction is a loop over the lane's own
+// 16 accumulators plus one exchange with lane l^32, and the exponentiated
+// block is already laid out as the B operand of O^T += V^T P^T.  K tiles are
+// staged in LDS row-major; V tiles are staged transposed (d x keys) with the
+// key order swizzled so each lane reads one 16-byte fragment per MFMA.
+// Global loads of tile j+1 are issued before tile j is computed and written
+// into the other LDS buffer afterwards (one barrier per tile).
+//
+// Causal: query tiles are launched heaviest first, key tiles past the
+// diagonal are never visited, 32-key blocks fully above a wave's rows are
+// skipped, and the mask is only evaluated on blocks that straddle the
+// diagonal or the ragged end of the sequence.
+//
+// Numerics: logits are accumulated in fp32 and scaled after the product
+// (an input is never pre-scaled); the softmax runs in base 2 with
+// scale*log2(e) folded into one FMA; O and l are rescaled when the running
+// max grows; O = acc / l and LSE = (m + log2 l) * ln 2 at the end.
+#include "fa2_common.hpp"
+#include "fa2_launch.hpp"
+
+namespace fa2 {
+
+template <typename T, int D>
+struct FwdTile {
+  static constexpr int NW = 4;
+  static constexpr int BR = 32 * NW;                   // query rows per workgroup
+  static constexpr int BC = sizeof(T) == 2 ? 64 : 32;  // keys per LDS tile
+  static constexpr int CH = Elt<T>::CH;
+  static constexpr int KS = D + CH;   // K tile row stride (elements, 16-byte pad)
+  static constexpr int VS = BC + CH;  // transposed V tile row stride
+  static constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-row output blocks over d
+  static constexpr int DCH = D / (2 * CH);         // chunks of a contraction over d
+  static constexpr int NJB = BC / 32;              // 32-key blocks per tile
+  static constexpr int CPB = 16 / CH;              // chunks per 32-key block
+  static constexpr int ROW_CH = D / CH;            // 16-byte chunks per row
+  static constexpr int K_CHUNKS = BC * ROW_CH;
+  static constexpr int K_PER_T = (K_CHUNKS + 255) / 256;
+  static constexpr int V_UNITS = (BC / 4) * ROW_CH;  // 4-row x CH-column units
+  static constexpr int V_PER_T = (V_UNITS + 255) / 256;
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                     const T* __restrict__ V, T* __restrict__ O,
+                                                     float* __restrict__ LSE, int N, int BH, int num_qt,
+                                                     float sl2) {
+  using C = FwdTile<T, D>;
+  constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
+  __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
+  __shared__ __attribute__((aligned(16))) T Vt[2][D * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int lin = blockIdx.x;
+  const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
+  const int bh = lin % BH;
+  const size_t base = (size_t)bh * N * D;
+  const T* Qh = Q + base;
+  const T* Kh = K + base;
+  const T* Vh = V + base;
+  const int q0 = qt * C::BR;
+  const int qw = q0 + 32 * w;  // first query row of this wave
+  const int qi = qw + l32;     // query row (column of S^T) owned by this lane
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds its query row, chunked over d.
+  u32x4 qf[C::DCH];
+#pragma unroll
+  for (int c = 0; c < C::DCH; ++c)
+    qf[c] = qi < N ? load16(Qh + (size_t)qi * D + c * 2 * CH + h * CH) : u32x4{0u, 0u, 0u, 0u};
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  u32x4 kr[C::K_PER_T];
+  u32x4 vr[C::V_PER_T][4];
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < C::K_PER_T; ++u) {
+      const int c = tid + 256 * u;
+      if (c < C::K_CHUNKS) {
+        const int j = kt * BC + c / C::ROW_CH;
+        kr[u] = j < N ? load16(Kh + (size_t)j * D + (c % C::ROW_CH) * CH) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < C::V_PER_T; ++s) {
+      const int uu = tid + 256 * s;
+      if (uu < C::V_UNITS) {
+        const int j0 = kt * BC + 4 * (uu / C::ROW_CH);
+        const int col = (uu % C::ROW_CH) * CH;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vr[s][e] = (j0 + e) < N ? load16(Vh + (size_t)(j0 + e) * D + col) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    T* ks = Ks[buf];
+    T* vt = Vt[buf];
+#pragma unroll
+    for (int u = 0; u < C::K_PER_T; ++u) {
+      const int c = tid + 256 * u;
+      if (c < C::K_CHUNKS) store16(ks + (c / C::ROW_CH) * KS + (c % C::ROW_CH) * CH, kr[u]);
+    }
+#pragma unroll
+    for (int s = 0; s < C::V_PER_T; ++s) {
+      const int uu = tid + 256 * s;
+      if (uu < C::V_UNITS)
+        write_transposed4<T>(vt, VS, (uu % C::ROW_CH) * CH, swap_bits23(4 * (uu / C::ROW_CH)), vr[s]);
+    }
+  };
+
+  f32x16 o[C::NB];
+#pragma unroll
+  for (int b = 0; b < C::NB; ++b) o[b] = f32x16{};
+  float m_run = -INFINITY;  // running max of scaled logits, base-2 units
+  float l_run = 0.f;        // this lane half's share of the running sum
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const bool more = kt + 1 < n_kt;
+    if (more) load_tile(kt + 1);
+    const T* ks = Ks[kt & 1];
+    const T* vt = Vt[kt & 1];
+    const int kb0 = kt * BC;
+    // 32-key blocks of this tile that hold a key this wave may see.
+    const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
+    const int nlive = last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1);
+
+    if (nlive > 0) {
+      f32x16 s[C::NJB];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < C::NJB; ++jb) {
+        if (jb < nlive) {
+          s[jb] = f32x16{};
+          const T* krow = ks + (32 * jb + l32) * KS + h * CH;
+#pragma unroll
+          for (int c = 0; c < C::DCH; ++c) mfma_chunk<T>(s[jb], load16(krow + c * 2 * CH), qf[c]);
+          const int kb = kb0 + 32 * jb;
+          if ((CAUSAL && kb + 31 > qw) || kb + 32 > N) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = kb + acc_row(r, h);
+              if ((CAUSAL && j > qi) || j >= N) s[jb][r] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b) o[b] *= alpha;
+
+#pragma unroll
+      for (int jb = 0; jb < C::NJB; ++jb) {
+        if (jb < nlive) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], sl2, -m_new));
+            s[jb][r] = p;
+            l_run += p;
+          }
+#pragma unroll
+          for (int t = 0; t < C::CPB; ++t) {
+            const u32x4 pb = pack_chunk<T>(s[jb], t);
+            const int pos = 32 * jb + chunk_pos<CH>(t, h);
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b) {
+              const int vrow = D >= 32 ? 32 * b + l32 : (l32 & (D - 1));
+              mfma_chunk<T>(o[b], load16(vt + vrow * VS + pos), pb);
+            }
+          }
+        }
+      }
+    }
+    if (more) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qi < N) {
+    const float inv = 1.0f / l_tot;
+    T* Oi = O + base + (size_t)qi * D;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * b + 8 * g + 4 * h;
+        if (d0 < D)
+          store4<T>(Oi + d0, o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
+                    o[b][4 * g + 3] * inv);
+      }
+    }
+    if (h == 0) LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a) {
+  using C = FwdTile<T, D>;
+  const int BH = a.B * a.H;
+  const int num_qt = (a.N + C::BR - 1) / C::BR;
+  const long long blocks = (long long)num_qt * BH;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float sl2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2);
+  return hipGetLastError();
+}
+
+template <typename T, bool CAUSAL>
+static hipError_t launch_fwd_d(const FwdArgs& a) {
+  switch (a.d) {
+    case 16: return launch_fwd_t<T, 16, CAUSAL>(a);
+    case 32: return launch_fwd_t<T, 32, CAUSAL>(a);
+    case 64: return launch_fwd_t<T, 64, CAUSAL>(a);
+    case 128: return launch_fwd_t<T, 128, CAUSAL>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_forward(const FwdArgs& a) {
+  if (a.dtype == kBF16)
+    return a.causal ? launch_fwd_d<__bf16, true>(a) : launch_fwd_d<__bf16, false>(a);
+  return a.causal ? launch_fwd_d<float, true>(a) : launch_fwd_d<float, false>(a);
+}
+
+}  // namespace fa2

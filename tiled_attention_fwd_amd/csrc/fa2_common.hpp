@@ -112,6 +112,28 @@ __device__ __forceinline__ u32x4 pack_chunk<float>(const f32x16& x, int t) {
   return as_u32x4(f32x4{x[4 * t], x[4 * t + 1], x[4 * t + 2], x[4 * t + 3]});
 }
 
+// acc + sum of the CH values of a packed fragment (bf16: v_dot2 with ones,
+// i.e. the sum of exactly the rounded weights the MFMA consumes).
+template <typename T>
+__device__ __forceinline__ float add_fragment_sum(float acc, u32x4 v);
+
+template <>
+__device__ __forceinline__ float add_fragment_sum<__bf16>(float acc, u32x4 v) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), one, acc, false);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float add_fragment_sum<float>(float acc, u32x4 v) {
+  const f32x4 f = as_f32x4(v);
+  return acc + ((f[0] + f[1]) + (f[2] + f[3]));
+}
+
 // Store 4 consecutive fp32 values as 4 elements of T (8 or 16 bytes).
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
@@ -167,6 +189,48 @@ __device__ __forceinline__ void write_transposed4<__bf16>(__bf16* tile, int row_
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A-operand fragment of chunk t for a product that contracts over the ROWS of
+// a row-major LDS tile (the transposed operand V^T, Q^T, dO^T, K^T, ...).
+// Lane (l32, h) supplies output row m = cb + l32 (a tile column) and the
+// contraction slots of chunk t of the 32-row block starting at tile row rb,
+// numbered exactly as pack_chunk numbers the accumulator rows it pairs with:
+//   bf16: slots 0-3 = rows rb+16t+4h+0..3, slots 4-7 = rows rb+16t+8+4h+0..3;
+//   fp32: slot e    = row  rb+8t+4h+e.
+// bf16 uses the gfx950 LDS transpose read ds_read_b64_tr_b16: inside each
+// 16-lane group, input lane j supplies the 8 bytes at row (j/4), columns
+// 4*(j%4)..+3 of a 4x16 block and output lane i receives column i of all four
+// rows.  Two such reads (rows +0..3 and +8..11) fill the 8 slots.  The bf16
+// tile needs cb+32 readable columns per row (padding may supply them); the
+// fp32 path reads column cb + (l32 & cmask) so narrow tiles stay in bounds.
+template <typename T>
+__device__ __forceinline__ u32x4 load_rowcontract(const T* tile, int stride, int rb, int t, int cb, int cmask,
+                                                  int lane);
+
+template <>
+__device__ __forceinline__ u32x4 load_rowcontract<__bf16>(const __bf16* tile, int stride, int rb, int t, int cb,
+                                                          int /*cmask*/, int lane) {
+  const int h = lane >> 5, j = lane & 15;
+  const int row = rb + 16 * t + 4 * h + (j >> 2);
+  const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const __bf16* p = tile + row * stride + col;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * stride));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(u32x4, both);
+}
+
+template <>
+__device__ __forceinline__ u32x4 load_rowcontract<float>(const float* tile, int stride, int rb, int t, int cb,
+                                                         int cmask, int lane) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const float* p = tile + (rb + 8 * t + 4 * h) * stride + cb + (l32 & cmask);
+  return as_u32x4(f32x4{p[0], p[stride], p[2 * stride], p[3 * stride]});
+}
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

@@ -13,12 +13,12 @@
 // computes the TRANSPOSED score block S^T = K Q^T (keys x queries) on MFMA,
 // so every lane owns one query column: its running max m and sum l are
 // plain per-lane registers, the row reduction is a loop over the lane's own
-// 16 accumulators plus one exchange with lane l^32, and the exponentiated
-// block is already laid out as the B operand of O^T += V^T P^T.  K tiles are
-// staged in LDS row-major; V tiles are staged transposed (d x keys) with the
-// key order swizzled so each lane reads one 16-byte fragment per MFMA.
-// Global loads of tile j+1 are issued before tile j is computed and written
-// into the other LDS buffer afterwards (one barrier per tile).
+// accumulators plus one exchange with lane l^32, and the exponentiated block
+// is already laid out as the B operand of O^T += V^T P^T.  K and V tiles are
+// staged row-major in LDS (global loads of tile j+1 are issued before tile j
+// is computed and land in the other buffer; one barrier per tile).  The V^T
+// operand is read with the gfx950 LDS transpose read, so nothing is ever
+// written transposed.
 //
 // Causal: query tiles are launched heaviest first, key tiles past the
 // diagonal are never visited, 32-key blocks fully above a wave's rows are
@@ -27,12 +27,16 @@
 //
 // Numerics: logits are accumulated in fp32 and scaled after the product
 // (an input is never pre-scaled); the softmax runs in base 2 with
-// scale*log2(e) folded into one FMA; O and l are rescaled when the running
-// max grows; O = acc / l and LSE = (m + log2 l) * ln 2 at the end.
+// scale*log2(e) folded into one FMA.  The running max only moves when the
+// block max exceeds it by more than kSlack (base-2 units), so the O rescale
+// is skipped in most tiles; weights are then at most 2^kSlack, harmless in
+// fp32 and bf16.  At the end O = acc / l and LSE = (m + log2 l) * ln 2.
 #include "fa2_common.hpp"
 #include "fa2_launch.hpp"
 
 namespace fa2 {
+
+constexpr float kSlack = 8.0f;
 
 template <typename T, int D>
 struct FwdTile {
@@ -40,17 +44,18 @@ struct FwdTile {
   static constexpr int BR = 32 * NW;                   // query rows per workgroup
   static constexpr int BC = sizeof(T) == 2 ? 64 : 32;  // keys per LDS tile
   static constexpr int CH = Elt<T>::CH;
-  static constexpr int KS = D + CH;   // K tile row stride (elements, 16-byte pad)
-  static constexpr int VS = BC + CH;  // transposed V tile row stride
+  static constexpr int KS = D + CH;  // K row stride: 16-byte pad, conflict-free row reads
+  // V row stride: bf16 transpose reads touch 4 consecutive rows per 16 lanes;
+  // a 32-byte pad puts those rows on disjoint banks.
+  static constexpr int VS = sizeof(T) == 2 ? D + 16 : D + 4;
   static constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-row output blocks over d
-  static constexpr int DCH = D / (2 * CH);         // chunks of a contraction over d
-  static constexpr int NJB = BC / 32;              // 32-key blocks per tile
-  static constexpr int CPB = 16 / CH;              // chunks per 32-key block
-  static constexpr int ROW_CH = D / CH;            // 16-byte chunks per row
-  static constexpr int K_CHUNKS = BC * ROW_CH;
-  static constexpr int K_PER_T = (K_CHUNKS + 255) / 256;
-  static constexpr int V_UNITS = (BC / 4) * ROW_CH;  // 4-row x CH-column units
-  static constexpr int V_PER_T = (V_UNITS + 255) / 256;
+  static constexpr int CMASK = (D >= 32 ? 32 : D) - 1;
+  static constexpr int DCH = D / (2 * CH);  // chunks of a contraction over d
+  static constexpr int NJB = BC / 32;       // 32-key blocks per tile
+  static constexpr int CPB = 16 / CH;       // chunks per 32-key block
+  static constexpr int ROW_CH = D / CH;     // 16-byte chunks per row
+  static constexpr int CHUNKS = BC * ROW_CH;
+  static constexpr int PER_T = (CHUNKS + 255) / 256;
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -61,7 +66,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   using C = FwdTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) T Vt[2][D * VS];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BC * VS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -76,52 +81,41 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds its query row, chunked over d.
+  // Q^T as the B operand of S^T = K Q^T: lane holds its query row, chunked
+  // over d.  Rows past N load row N-1 (finite) and are never stored.
   u32x4 qf[C::DCH];
+  {
+    const T* qrow = Qh + (size_t)min(qi, N - 1) * D + h * CH;
 #pragma unroll
-  for (int c = 0; c < C::DCH; ++c)
-    qf[c] = qi < N ? load16(Qh + (size_t)qi * D + c * 2 * CH + h * CH) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < C::DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
+  }
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  u32x4 kr[C::K_PER_T];
-  u32x4 vr[C::V_PER_T][4];
-
+  // Tile loads: rows past N load row N-1; those keys are masked to -inf, so
+  // their (finite) values never reach the output.
+  u32x4 kr[C::PER_T], vr[C::PER_T];
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < C::K_PER_T; ++u) {
+    for (int u = 0; u < C::PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::K_CHUNKS) {
-        const int j = kt * BC + c / C::ROW_CH;
-        kr[u] = j < N ? load16(Kh + (size_t)j * D + (c % C::ROW_CH) * CH) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < C::V_PER_T; ++s) {
-      const int uu = tid + 256 * s;
-      if (uu < C::V_UNITS) {
-        const int j0 = kt * BC + 4 * (uu / C::ROW_CH);
-        const int col = (uu % C::ROW_CH) * CH;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vr[s][e] = (j0 + e) < N ? load16(Vh + (size_t)(j0 + e) * D + col) : u32x4{0u, 0u, 0u, 0u};
+      if (c < C::CHUNKS) {
+        const size_t off = (size_t)min(kt * BC + c / C::ROW_CH, N - 1) * D + (c % C::ROW_CH) * CH;
+        kr[u] = load16(Kh + off);
+        vr[u] = load16(Vh + off);
       }
     }
   };
   auto store_tile = [&](int buf) {
-    T* ks = Ks[buf];
-    T* vt = Vt[buf];
 #pragma unroll
-    for (int u = 0; u < C::K_PER_T; ++u) {
+    for (int u = 0; u < C::PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::K_CHUNKS) store16(ks + (c / C::ROW_CH) * KS + (c % C::ROW_CH) * CH, kr[u]);
-    }
-#pragma unroll
-    for (int s = 0; s < C::V_PER_T; ++s) {
-      const int uu = tid + 256 * s;
-      if (uu < C::V_UNITS)
-        write_transposed4<T>(vt, VS, (uu % C::ROW_CH) * CH, swap_bits23(4 * (uu / C::ROW_CH)), vr[s]);
+      if (c < C::CHUNKS) {
+        const int row = c / C::ROW_CH, col = (c % C::ROW_CH) * CH;
+        store16(&Ks[buf][row * KS + col], kr[u]);
+        store16(&Vs[buf][row * VS + col], vr[u]);
+      }
     }
   };
 
@@ -139,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     const bool more = kt + 1 < n_kt;
     if (more) load_tile(kt + 1);
     const T* ks = Ks[kt & 1];
-    const T* vt = Vt[kt & 1];
+    const T* vs = Vs[kt & 1];
     const int kb0 = kt * BC;
     // 32-key blocks of this tile that hold a key this wave may see.
     const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
@@ -147,7 +141,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
 
     if (nlive > 0) {
       f32x16 s[C::NJB];
-      float mx = -INFINITY;
 #pragma unroll
       for (int jb = 0; jb < C::NJB; ++jb) {
         if (jb < nlive) {
@@ -155,6 +148,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
           const T* krow = ks + (32 * jb + l32) * KS + h * CH;
 #pragma unroll
           for (int c = 0; c < C::DCH; ++c) mfma_chunk<T>(s[jb], load16(krow + c * 2 * CH), qf[c]);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < C::NJB; ++jb) {
+        if (jb < nlive) {
           const int kb = kb0 + 32 * jb;
           if ((CAUSAL && kb + 31 > qw) || kb + 32 > N) {
 #pragma unroll
@@ -164,35 +163,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
             }
           }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[jb][r], s[jb][r + 1]));
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      const float m_cand = mx * sl2;
+      const bool grow = m_cand > m_run + kSlack;
+      if (__any(grow)) {
+        const float m_new = grow ? m_cand : m_run;
+        // 0 on a lane's first visible keys; exactly 1 where the max stays.
+        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int b = 0; b < C::NB; ++b) o[b] *= alpha;
+        for (int b = 0; b < C::NB; ++b) o[b] *= alpha;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
 
 #pragma unroll
       for (int jb = 0; jb < C::NJB; ++jb) {
         if (jb < nlive) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], sl2, -m_new));
-            s[jb][r] = p;
-            l_run += p;
-          }
+          for (int r = 0; r < 16; ++r) s[jb][r] = __builtin_amdgcn_exp2f(fmaf(s[jb][r], sl2, neg_m));
 #pragma unroll
           for (int t = 0; t < C::CPB; ++t) {
             const u32x4 pb = pack_chunk<T>(s[jb], t);
-            const int pos = 32 * jb + chunk_pos<CH>(t, h);
+            l_run = add_fragment_sum<T>(l_run, pb);
 #pragma unroll
-            for (int b = 0; b < C::NB; ++b) {
-              const int vrow = D >= 32 ? 32 * b + l32 : (l32 & (D - 1));
-              mfma_chunk<T>(o[b], load16(vt + vrow * VS + pos), pb);
-            }
+            for (int b = 0; b < C::NB; ++b)
+              mfma_chunk<T>(o[b], load_rowcontract<T>(vs, VS, 32 * jb, t, 32 * b, C::CMASK, lane), pb);
           }
         }
       }

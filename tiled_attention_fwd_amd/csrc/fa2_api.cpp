@@ -78,11 +78,8 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   const size_t rows = (size_t)B * H * N;
   if (!workspace || workspace_bytes < fa2::ws_total_bytes(rows, d, dtype)) return FA2_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
-  char* ws = static_cast<char*>(workspace);
-  float* delta = reinterpret_cast<float*>(ws);
-  float* dq_acc = dtype == FA2_BF16 ? reinterpret_cast<float*>(ws + fa2::ws_delta_bytes(rows))
-                                    : static_cast<float*>(dq);
-  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, delta, dq_acc,
+  float* delta = static_cast<float*>(workspace);
+  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, delta,
                  static_cast<hipStream_t>(stream)};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;

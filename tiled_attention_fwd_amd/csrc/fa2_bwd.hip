@@ -13,21 +13,25 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Kernels, in stream order:
-//   bwd_pre_kernel   D = rowsum(dO o O) in fp32, and zeroing of the fp32 dQ
-//                    accumulator (HBM-bound, one pass over O and dO).
-//   bwd_kernel       one workgroup per (batch, head, 128-key tile); each of
+//   bwd_pre_kernel   D = rowsum(dO o O) in fp32 (HBM-bound, one pass over O
+//                    and dO).
+//   bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile); each of
 //                    its 4 waves owns 32 keys and keeps K, V (as MFMA B
 //                    operands) and its dK^T, dV^T accumulators in registers
-//                    while it walks the query tiles.  Per query tile:
-//                    S = Q K^T and dP = dO V^T on MFMA, P and dS in fp32,
-//                    dV^T += dO^T P and dK^T += Q^T dS on MFMA (P and dS feed
-//                    straight from the accumulator layout; Q and dO are also
-//                    staged transposed in LDS), then dS goes through LDS and
-//                    dQ_tile = dS K is computed on MFMA and added into the
-//                    fp32 accumulator with atomics.
-//   dq_convert_kernel  fp32 accumulator -> bf16 dQ (bf16 mode only).
-// Causal: key tiles start at the first query tile that can see them and
-// launch heaviest first; blocks entirely above the diagonal are skipped.
+//                    while it walks the query tiles: S = Q K^T and
+//                    dP = dO V^T on MFMA, P and dS in fp32, then
+//                    dV^T += dO^T P and dK^T += Q^T dS on MFMA, with P and dS
+//                    fed straight from the accumulator layout and Q^T, dO^T
+//                    read from the row-major LDS tiles by transpose reads.
+//   bwd_dq_kernel    one workgroup per (batch, head, 128-query tile), shaped
+//                    like the forward pass: S^T = K Q^T and dP^T = V dO^T on
+//                    MFMA, so each lane owns one query and its LSE and D are
+//                    scalars, then dQ^T += K^T dS^T.
+// The two halves recompute S and dP instead of exchanging dS, so dQ needs no
+// atomics or fp32 accumulator and the result is deterministic.
+// Causal: tiles start and stop at the diagonal, blocks entirely above it
+// are skipped, and only blocks that straddle it (or the ragged end of the
+// sequence) evaluate the mask.
 #include "fa2_common.hpp"
 #include "fa2_launch.hpp"
 
@@ -59,11 +63,10 @@ __device__ __forceinline__ float dot_chunk<__bf16>(u32x4 a, u32x4 b) {
   return s;
 }
 
-// D_i = sum_k dO_ik O_ik; optionally zero row i of the fp32 dQ accumulator.
+// D_i = sum_k dO_ik O_ik.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                      float* __restrict__ Delta, float* __restrict__ dQacc,
-                                                      long long rows) {
+                                                      float* __restrict__ Delta, long long rows) {
   constexpr int CH = Elt<T>::CH;
   constexpr int TPR = D / CH;  // threads per row (2..32, a power of two)
   constexpr int RPB = 256 / TPR;
@@ -72,70 +75,49 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
   float acc = 0.f;
   if (row < rows) {
     acc = dot_chunk<T>(load16(O + row * D + cc * CH), load16(dO + row * D + cc * CH));
-    float* z = dQacc + row * D + cc * CH;
-#pragma unroll
-    for (int k = 0; k < CH / 4; ++k) store16(z + 4 * k, u32x4{0u, 0u, 0u, 0u});
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && cc == 0) Delta[row] = acc;
 }
 
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,
-                                                         long long n8) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
-    const f32x4 lo = as_f32x4(load16(acc + 8 * i)), hi = as_f32x4(load16(acc + 8 * i + 4));
-    const f32x2 p0 = {lo[0], lo[1]}, p1 = {lo[2], lo[3]}, p2 = {hi[0], hi[1]}, p3 = {hi[2], hi[3]};
-    const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2)),
-                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2)),
-                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2)),
-                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p3, bf16x2))};
-    store16(dq + 8 * i, r);
-  }
-}
-
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (batch, head, 128-key tile).
+// ---------------------------------------------------------------------------
 template <typename T, int D>
-struct BwdTile {
+struct DkdvTile {
   static constexpr int NW = 4;
   static constexpr int BC = 32 * NW;  // keys per workgroup
-  static constexpr int MB = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+  static constexpr int MB = (sizeof(T) == 4 && D >= 64) ? 1 : 2;
   static constexpr int BR = 32 * MB;  // query rows per iteration
   static constexpr int CH = Elt<T>::CH;
-  static constexpr int QS = D + CH;    // natural Q / dO tile row stride
-  static constexpr int TS = BR + CH;   // transposed Q / dO tile row stride
-  static constexpr int SS = BC + CH;   // dS tile row stride
-  static constexpr int KTS = BC + CH;  // transposed K tile row stride
+  static constexpr int EPW = 4 / sizeof(T);  // elements per 4-byte word
+  // Q and dO tiles are read row-wise (S, dP) and through transpose reads
+  // (dK, dV); bf16 transpose reads of a 32-column block touch columns up to
+  // 31, so even a 16-wide tile gets rows of at least 32 elements.
+  static constexpr int QS = lds_stride_words((D >= 32 ? D : 32) / EPW) * EPW;
   static constexpr int NB = D >= 32 ? D / 32 : 1;
+  static constexpr int CMASK = (D >= 32 ? 32 : D) - 1;
   static constexpr int DCH = D / (2 * CH);
   static constexpr int CPB = 16 / CH;
   static constexpr int ROW_CH = D / CH;
-  static constexpr int T_UNITS = (BR / 4) * ROW_CH;
-  static constexpr int T_PER_T = (T_UNITS + 255) / 256;
-  static constexpr int K_UNITS = (BC / 4) * ROW_CH;
-  static constexpr int K_PER_T = (K_UNITS + 255) / 256;
-  static constexpr int SCH = BC / (2 * CH);  // chunks of the dQ contraction over keys
-  static constexpr int NQB = MB * NB;        // 32x32 dQ output blocks per query tile
-  static constexpr int QB_PER_W = (NQB + NW - 1) / NW;
+  static constexpr int Q_CHUNKS = BR * ROW_CH;
+  static constexpr int Q_PER_T = (Q_CHUNKS + 255) / 256;
+  static constexpr int OCC = (sizeof(T) == 2 && D <= 64) ? 2 : 1;  // workgroups per CU the registers allow
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                     const T* __restrict__ V, const T* __restrict__ dO,
-                                                     const float* __restrict__ LSE,
-                                                     const float* __restrict__ Delta, float* __restrict__ dQacc,
-                                                     T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
-                                                     float sl2, float scale) {
-  using C = BwdTile<T, D>;
-  constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB;
-  constexpr int QS = C::QS, TS = C::TS, SS = C::SS, KTS = C::KTS;
-  __shared__ __attribute__((aligned(16))) T Qs[BR * QS];
-  __shared__ __attribute__((aligned(16))) T dOs[BR * QS];
-  __shared__ __attribute__((aligned(16))) T Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) T dOt[D * TS];
-  __shared__ __attribute__((aligned(16))) T dSs[BR * SS];
-  __shared__ __attribute__((aligned(16))) T Kt[D * KTS];
-  __shared__ float lse_s[BR];
-  __shared__ float dl_s[BR];
+__global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int N,
+    int BH, float sl2, float scale) {
+  using C = DkdvTile<T, D>;
+  constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB, QS = C::QS;
+  // Double-buffered query-side tiles: one barrier per query tile.
+  __shared__ __attribute__((aligned(16))) T Qs[2][BR * QS];
+  __shared__ __attribute__((aligned(16))) T dOs[2][BR * QS];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BR];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][BR];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -144,8 +126,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const T* __restrict__ Q, co
   const int bh = lin % BH;
   const size_t base = (size_t)bh * N * D;
   const T* Qh = Q + base;
-  const T* Kh = K + base;
-  const T* Vh = V + base;
   const T* dOh = dO + base;
   const float* lseh = LSE + (size_t)bh * N;
   const float* dlh = Delta + (size_t)bh * N;
@@ -153,26 +133,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const T* __restrict__ Q, co
   const int kw = kv0 + 32 * w;  // first key of this wave
   const int kj = kw + l32;      // key (accumulator column) owned by this lane
 
-  // K and V rows of this lane as B operands of S = Q K^T and dP = dO V^T.
+  // K and V rows of this lane as B operands of S = Q K^T and dP = dO V^T
+  // (rows past N load row N-1; their weights are masked to 0).
   u32x4 kf[C::DCH], vf[C::DCH];
+  {
+    const size_t off = base + (size_t)min(kj, N - 1) * D + h * CH;
 #pragma unroll
-  for (int c = 0; c < C::DCH; ++c) {
-    const int col = c * 2 * CH + h * CH;
-    kf[c] = kj < N ? load16(Kh + (size_t)kj * D + col) : u32x4{0u, 0u, 0u, 0u};
-    vf[c] = kj < N ? load16(Vh + (size_t)kj * D + col) : u32x4{0u, 0u, 0u, 0u};
-  }
-  // K tile transposed (d x keys, natural key order) for dQ = dS K.
-#pragma unroll
-  for (int u = 0; u < C::K_PER_T; ++u) {
-    const int uu = tid + 256 * u;
-    if (uu < C::K_UNITS) {
-      const int j0 = kv0 + 4 * (uu / C::ROW_CH);
-      const int col = (uu % C::ROW_CH) * CH;
-      u32x4 r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r[e] = (j0 + e) < N ? load16(Kh + (size_t)(j0 + e) * D + col) : u32x4{0u, 0u, 0u, 0u};
-      write_transposed4<T>(Kt, KTS, col, 4 * (uu / C::ROW_CH), r);
+    for (int c = 0; c < C::DCH; ++c) {
+      kf[c] = load16(K + off + c * 2 * CH);
+      vf[c] = load16(V + off + c * 2 * CH);
     }
   }
 
@@ -186,21 +155,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const T* __restrict__ Q, co
   const int n_qt = (N + BR - 1) / BR;
   const int qt_begin = CAUSAL ? kv0 / BR : 0;
 
-  u32x4 qr[C::T_PER_T][4], gr[C::T_PER_T][4];
+  u32x4 qr[C::Q_PER_T], gr[C::Q_PER_T];
   float lr = 0.f, dr = 0.f;
   auto load_q = [&](int qt) {
 #pragma unroll
-    for (int s = 0; s < C::T_PER_T; ++s) {
-      const int uu = tid + 256 * s;
-      if (uu < C::T_UNITS) {
-        const int i0 = qt * BR + 4 * (uu / C::ROW_CH);
-        const int col = (uu % C::ROW_CH) * CH;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = (i0 + e) < N;
-          qr[s][e] = ok ? load16(Qh + (size_t)(i0 + e) * D + col) : u32x4{0u, 0u, 0u, 0u};
-          gr[s][e] = ok ? load16(dOh + (size_t)(i0 + e) * D + col) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int u = 0; u < C::Q_PER_T; ++u) {
+      const int c = tid + 256 * u;
+      if (c < C::Q_CHUNKS) {
+        const size_t off = (size_t)min(qt * BR + c / C::ROW_CH, N - 1) * D + (c % C::ROW_CH) * CH;
+        qr[u] = load16(Qh + off);
+        gr[u] = load16(dOh + off);
       }
     }
     if (tid < BR) {
@@ -209,113 +173,84 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const T* __restrict__ Q, co
       dr = i < N ? dlh[i] : 0.f;
     }
   };
-  auto store_q = [&]() {
+  auto store_q = [&](int buf) {
 #pragma unroll
-    for (int s = 0; s < C::T_PER_T; ++s) {
-      const int uu = tid + 256 * s;
-      if (uu < C::T_UNITS) {
-        const int rq = uu / C::ROW_CH;
-        const int col = (uu % C::ROW_CH) * CH;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          store16(Qs + (4 * rq + e) * QS + col, qr[s][e]);
-          store16(dOs + (4 * rq + e) * QS + col, gr[s][e]);
-        }
-        write_transposed4<T>(Qt, TS, col, swap_bits23(4 * rq), qr[s]);
-        write_transposed4<T>(dOt, TS, col, swap_bits23(4 * rq), gr[s]);
+    for (int u = 0; u < C::Q_PER_T; ++u) {
+      const int c = tid + 256 * u;
+      if (c < C::Q_CHUNKS) {
+        const int row = c / C::ROW_CH, col = (c % C::ROW_CH) * CH;
+        store16(&Qs[buf][row * QS + col], qr[u]);
+        store16(&dOs[buf][row * QS + col], gr[u]);
       }
     }
     if (tid < BR) {
-      lse_s[tid] = lr;
-      dl_s[tid] = dr;
+      lse_s[buf][tid] = lr;
+      dl_s[buf][tid] = dr;
     }
   };
 
-  if (qt_begin < n_qt) load_q(qt_begin);
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    store_q();
-    __syncthreads();
-    if (qt + 1 < n_qt) load_q(qt + 1);
+  if (qt_begin < n_qt) {
+    load_q(qt_begin);
+    store_q(0);
+    if (qt_begin + 1 < n_qt) load_q(qt_begin + 1);
+  }
+  __syncthreads();
+
+  // A buffer is rewritten (store_q) one tile after its last reads, and every
+  // wave has passed the barrier that follows those reads by then.
+  const bool key_tail = kw + 31 >= N;  // this wave's keys reach past N
+  for (int qt = qt_begin, it = 0; qt < n_qt; ++qt, ++it) {
+    const int buf = it & 1;
+    const T* qs = Qs[buf];
+    const T* gs = dOs[buf];
+    const float* ls = lse_s[buf];
+    const float* ds = dl_s[buf];
     const int i0 = qt * BR;
 
-    f32x16 s[MB], dp[MB];
-    bool live[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int ib = i0 + 32 * mb;
-      live[mb] = kw < N && ib < N && (!CAUSAL || ib + 31 >= kw);
-      if (live[mb]) {
-        s[mb] = f32x16{};
-        dp[mb] = f32x16{};
-        const T* qrow = Qs + (32 * mb + l32) * QS + h * CH;
-        const T* grow = dOs + (32 * mb + l32) * QS + h * CH;
+      if (kw < N && ib < N && (!CAUSAL || ib + 31 >= kw)) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const T* qrow = qs + (32 * mb + l32) * QS + h * CH;
+        const T* grow = gs + (32 * mb + l32) * QS + h * CH;
 #pragma unroll
         for (int c = 0; c < C::DCH; ++c) {
-          mfma_chunk<T>(s[mb], load16(qrow + c * 2 * CH), kf[c]);
-          mfma_chunk<T>(dp[mb], load16(grow + c * 2 * CH), vf[c]);
+          mfma_chunk<T>(s, load16(qrow + c * 2 * CH), kf[c]);
+          mfma_chunk<T>(dp, load16(grow + c * 2 * CH), vf[c]);
         }
+        const bool need_mask = (CAUSAL && ib < kw + 31) || key_tail;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int il = 32 * mb + acc_row(r, h);
-          const int i = i0 + il;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], sl2, -lse_s[il]));
-          if ((CAUSAL && kj > i) || kj >= N) p = 0.f;
-          s[mb][r] = p;
-          dp[mb][r] = p * (dp[mb][r] - dl_s[il]);
+        for (int g = 0; g < 4; ++g) {
+          const int il = 32 * mb + 8 * g + 4 * h;  // rows il..il+3 of this lane
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + il);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + il);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * g + q;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
+            if (need_mask && ((CAUSAL && kj > i0 + il + q) || kj >= N)) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[q]);
+          }
         }
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the query rows).
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (live[mb]) {
+        // dV^T += dO^T P and dK^T += Q^T dS (contraction over the query rows,
+        // the transposed operands read straight from the row-major tiles).
 #pragma unroll
         for (int t = 0; t < C::CPB; ++t) {
-          const u32x4 pb = pack_chunk<T>(s[mb], t);
-          const u32x4 sb = pack_chunk<T>(dp[mb], t);
-          const int pos = 32 * mb + chunk_pos<CH>(t, h);
+          const u32x4 pb = pack_chunk<T>(s, t);
+          const u32x4 sb = pack_chunk<T>(dp, t);
 #pragma unroll
           for (int b = 0; b < C::NB; ++b) {
-            const int trow = D >= 32 ? 32 * b + l32 : (l32 & (D - 1));
-            mfma_chunk<T>(dv[b], load16(dOt + trow * TS + pos), pb);
-            mfma_chunk<T>(dk[b], load16(Qt + trow * TS + pos), sb);
+            mfma_chunk<T>(dv[b], load_rowcontract<T>(gs, QS, 32 * mb, t, 32 * b, C::CMASK, lane), pb);
+            mfma_chunk<T>(dk[b], load_rowcontract<T>(qs, QS, 32 * mb, t, 32 * b, C::CMASK, lane), sb);
           }
         }
       }
     }
-    // dS of this wave's 32 keys into the shared tile (zeros where skipped).
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        dSs[(32 * mb + acc_row(r, h)) * SS + 32 * w + l32] = live[mb] ? from_f32<T>(dp[mb][r]) : from_f32<T>(0.f);
-    }
+    if (qt + 1 < n_qt) store_q(buf ^ 1);
     __syncthreads();
-    // dQ_tile = dS (BR x BC) K (BC x D), added into the fp32 accumulator.
-#pragma unroll
-    for (int u = 0; u < C::QB_PER_W; ++u) {
-      const int bidx = w + C::NW * u;
-      if (bidx < C::NQB) {
-        const int mb = bidx / C::NB, b = bidx % C::NB;
-        const int ib = i0 + 32 * mb;
-        if (ib < N && (!CAUSAL || ib + 31 >= kv0)) {
-          f32x16 acc = f32x16{};
-          const T* arow = dSs + (32 * mb + l32) * SS + h * CH;
-          const T* brow = Kt + (D >= 32 ? 32 * b + l32 : (l32 & (D - 1))) * KTS + h * CH;
-#pragma unroll
-          for (int c = 0; c < C::SCH; ++c) mfma_chunk<T>(acc, load16(arow + c * 2 * CH), load16(brow + c * 2 * CH));
-          const int dcol = 32 * b + l32;
-          if (dcol < D) {
-            float* dst = dQacc + base + dcol;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = ib + acc_row(r, h);
-              if (i < N) unsafeAtomicAdd(dst + (size_t)i * D, acc[r] * scale);
-            }
-          }
-        }
-      }
-    }
+    if (qt + 2 < n_qt) load_q(qt + 2);
   }
 
   if (kj < N) {
@@ -336,34 +271,193 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const T* __restrict__ Q, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (batch, head, 128-query tile).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DqTile {
+  static constexpr int NW = 4;
+  static constexpr int BR = 32 * NW;                   // query rows per workgroup
+  static constexpr int BC = sizeof(T) == 2 ? 64 : 32;  // keys per LDS tile
+  static constexpr int CH = Elt<T>::CH;
+  static constexpr int EPW = 4 / sizeof(T);
+  // K is read row-wise (S^T) and through transpose reads (dQ^T); V only
+  // row-wise (dP^T), which a 16-byte pad keeps conflict-free.
+  static constexpr int KS = lds_stride_words((D >= 32 ? D : 32) / EPW) * EPW;
+  static constexpr int VS = D + CH;
+  static constexpr int NB = D >= 32 ? D / 32 : 1;
+  static constexpr int CMASK = (D >= 32 ? 32 : D) - 1;
+  static constexpr int DCH = D / (2 * CH);
+  static constexpr int NJB = BC / 32;
+  static constexpr int CPB = 16 / CH;
+  static constexpr int ROW_CH = D / CH;
+  static constexpr int CHUNKS = BC * ROW_CH;
+  static constexpr int PER_T = (CHUNKS + 255) / 256;
+  static constexpr int OCC = (sizeof(T) == 4 && D == 128) ? 1 : 2;  // workgroups per CU
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                        const T* __restrict__ V, const T* __restrict__ dO,
+                                                        const float* __restrict__ LSE,
+                                                        const float* __restrict__ Delta, T* __restrict__ dQ, int N,
+                                                        int BH, int num_qt, float sl2, float scale) {
+  using C = DqTile<T, D>;
+  constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
+  __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BC * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int lin = blockIdx.x;
+  const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
+  const int bh = lin % BH;
+  const size_t base = (size_t)bh * N * D;
+  const T* Kh = K + base;
+  const T* Vh = V + base;
+  const int q0 = qt * C::BR;
+  const int qw = q0 + 32 * w;  // first query row of this wave
+  const int qi = qw + l32;     // query row (column of S^T) owned by this lane
+
+  // Q and dO rows of this lane (B operands); its LSE (base 2) and D.  Rows
+  // past N read row N-1 and are never stored.
+  const int qc = min(qi, N - 1);
+  u32x4 qf[C::DCH], gf[C::DCH];
+  {
+    const size_t off = base + (size_t)qc * D + h * CH;
+#pragma unroll
+    for (int c = 0; c < C::DCH; ++c) {
+      qf[c] = load16(Q + off + c * 2 * CH);
+      gf[c] = load16(dO + off + c * 2 * CH);
+    }
+  }
+  const float lse2 = LSE[(size_t)bh * N + qc] * kLog2e;
+  const float dl = Delta[(size_t)bh * N + qc];
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  u32x4 kr[C::PER_T], vr[C::PER_T];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < C::PER_T; ++u) {
+      const int c = tid + 256 * u;
+      if (c < C::CHUNKS) {
+        const size_t off = (size_t)min(kt * BC + c / C::ROW_CH, N - 1) * D + (c % C::ROW_CH) * CH;
+        kr[u] = load16(Kh + off);
+        vr[u] = load16(Vh + off);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < C::PER_T; ++u) {
+      const int c = tid + 256 * u;
+      if (c < C::CHUNKS) {
+        const int row = c / C::ROW_CH, col = (c % C::ROW_CH) * CH;
+        store16(&Ks[buf][row * KS + col], kr[u]);
+        store16(&Vs[buf][row * VS + col], vr[u]);
+      }
+    }
+  };
+
+  f32x16 dq[C::NB];
+#pragma unroll
+  for (int b = 0; b < C::NB; ++b) dq[b] = f32x16{};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const bool more = kt + 1 < n_kt;
+    if (more) load_tile(kt + 1);
+    const T* ks = Ks[kt & 1];
+    const T* vs = Vs[kt & 1];
+    const int kb0 = kt * BC;
+    const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
+    const int nlive = last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1);
+#pragma unroll
+    for (int jb = 0; jb < C::NJB; ++jb) {
+      if (jb < nlive) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const T* krow = ks + (32 * jb + l32) * KS + h * CH;
+        const T* vrow = vs + (32 * jb + l32) * VS + h * CH;
+#pragma unroll
+        for (int c = 0; c < C::DCH; ++c) {
+          mfma_chunk<T>(s, load16(krow + c * 2 * CH), qf[c]);
+          mfma_chunk<T>(dp, load16(vrow + c * 2 * CH), gf[c]);
+        }
+        const int kb = kb0 + 32 * jb;
+        const bool need_mask = (CAUSAL && kb + 31 > qw) || kb + 32 > N;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+          if (need_mask) {
+            const int j = kb + acc_row(r, h);
+            if ((CAUSAL && j > qi) || j >= N) p = 0.f;
+          }
+          dp[r] = p * (dp[r] - dl);
+        }
+        // dQ^T += K^T dS^T: K^T through transpose reads of the key tile.
+#pragma unroll
+        for (int t = 0; t < C::CPB; ++t) {
+          const u32x4 sb = pack_chunk<T>(dp, t);
+#pragma unroll
+          for (int b = 0; b < C::NB; ++b)
+            mfma_chunk<T>(dq[b], load_rowcontract<T>(ks, KS, 32 * jb, t, 32 * b, C::CMASK, lane), sb);
+        }
+      }
+    }
+    if (more) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qi < N) {
+    T* dQi = dQ + base + (size_t)qi * D;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * b + 8 * g + 4 * h;
+        if (d0 < D)
+          store4<T>(dQi + d0, dq[b][4 * g] * scale, dq[b][4 * g + 1] * scale, dq[b][4 * g + 2] * scale,
+                    dq[b][4 * g + 3] * scale);
+      }
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
-  using C = BwdTile<T, D>;
   const int BH = a.B * a.H;
   const long long rows = (long long)BH * a.N;
+  const float sl2 = a.scale * kLog2e;
   if (stage == 1) {
     constexpr int RPB = 256 / (D / Elt<T>::CH);
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.delta, a.dq_acc,
-                       rows);
+                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.delta, rows);
     return hipGetLastError();
   }
   if (stage == 2) {
+    using C = DkdvTile<T, D>;
     const long long blocks = (long long)((a.N + C::BC - 1) / C::BC) * BH;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dO), a.lse, a.delta, a.dq_acc, static_cast<T*>(a.dk),
-                       static_cast<T*>(a.dv), a.N, BH, a.scale * kLog2e, a.scale);
+                       static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                       a.N, BH, sl2, a.scale);
     return hipGetLastError();
   }
   if (stage == 3) {
-    if (a.dtype != kBF16) return hipSuccess;  // fp32 mode accumulates into dq directly
-    const long long n8 = rows * D / 8;
-    long long g = (n8 + 255) / 256;
-    if (g > 65536) g = 65536;
-    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)g), dim3(256), 0, a.stream, a.dq_acc,
-                       static_cast<__bf16*>(a.dq), n8);
+    using C = DqTile<T, D>;
+    const int num_qt = (a.N + C::BR - 1) / C::BR;
+    const long long blocks = (long long)num_qt * BH;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dq), a.N, BH, num_qt, sl2,
+                       a.scale);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -190,6 +190,26 @@ __device__ __forceinline__ void write_transposed4<__bf16>(__bf16* tile, int row_
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Row stride (in 4-byte words) for an LDS tile whose rows hold `row_words`
+// words and that is read both ways: 16 lanes reading 16 B from 16
+// consecutive rows (row-contiguous MFMA operands) need (stride/4) odd, so the
+// rows start on 16 distinct 4-bank groups of the 64 banks; 16 lanes of a
+// transpose read touch 4 consecutive rows x 8 words, which need the four
+// 8-bank windows stride*k mod 64 (k = 0..3) to be disjoint.  Returns the
+// smallest stride >= row_words meeting both.
+constexpr int lds_stride_words(int row_words) {
+  for (int s = row_words;; ++s) {
+    if (s % 4 != 0 || (s / 4) % 2 == 0) continue;
+    bool ok = true;
+    for (int a = 0; a < 4 && ok; ++a)
+      for (int b = a + 1; b < 4 && ok; ++b) {
+        const int d = ((s * b - s * a) % 64 + 64) % 64;
+        if (d < 8 || d > 56) ok = false;
+      }
+    if (ok) return s;
+  }
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // A-operand fragment of chunk t for a product that contracts over the ROWS of

@@ -40,20 +40,15 @@ struct BwdArgs {
   bool causal;
   int dtype;
   float* delta;  // [B, H, N] inside the workspace
-  float* dq_acc;  // [B, H, N, d] fp32 accumulator (dq itself in fp32 mode)
   hipStream_t stream;
 };
 
-// Workspace layout: delta first, then (bf16 mode) the fp32 dQ accumulator,
-// each section starting on a 256-byte boundary.
+// Workspace layout: D = rowsum(dO * O) as float [B, H, N], padded to 256 B.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t ws_delta_bytes(size_t rows) { return align256(rows * sizeof(float)); }
-inline size_t ws_total_bytes(size_t rows, int d, int dtype) {
-  return ws_delta_bytes(rows) + (dtype == kBF16 ? align256(rows * (size_t)d * sizeof(float)) : 0);
-}
+inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return align256(rows * sizeof(float)); }
 
 hipError_t launch_forward(const FwdArgs& a);
-// stage 1: D and accumulator zeroing; 2: the key-tile kernel; 3: dQ to bf16.
+// stage 1: D = rowsum(dO * O); 2: the dK/dV kernel; 3: the dQ kernel.
 hipError_t launch_backward_stage(const BwdArgs& a, int stage);
 
 }  // namespace fa2

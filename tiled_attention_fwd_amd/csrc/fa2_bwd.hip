@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   // A buffer is rewritten (store_q) one tile after its last reads, and every
   // wave has passed the barrier that follows those reads by then.
   const bool key_tail = kw + 31 >= N;  // this wave's keys reach past N
-  for (int qt = qt_begin, it = 0; qt < n_qt; ++qt, ++it) {
+  auto iteration = [&](int qt, int it, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int buf = it & 1;
     const T* qs = Qs[buf];
     const T* gs = dOs[buf];
@@ -219,7 +220,8 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
           mfma_chunk<T>(s, load16(qrow + c * 2 * CH), kf[c]);
           mfma_chunk<T>(dp, load16(grow + c * 2 * CH), vf[c]);
         }
-        const bool need_mask = (CAUSAL && ib < kw + 31) || key_tail;
+        // P = exp2(S*scale*log2e - LSE2) and dS = P (dP - D); rows past N
+        // have LSE2 = +inf and so P = 0.
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int il = 32 * mb + 8 * g + 4 * h;  // rows il..il+3 of this lane
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
           for (int q = 0; q < 4; ++q) {
             const int r = 4 * g + q;
             float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
-            if (need_mask && ((CAUSAL && kj > i0 + il + q) || kj >= N)) p = 0.f;
+            if (MASKED && ((CAUSAL && kj > i0 + il + q) || kj >= N)) p = 0.f;
             s[r] = p;
             dp[r] = p * (dp[r] - d4[q]);
           }
@@ -251,7 +253,13 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     if (qt + 1 < n_qt) store_q(buf ^ 1);
     __syncthreads();
     if (qt + 2 < n_qt) load_q(qt + 2);
-  }
+  };
+  // Query tiles that cross this key tile's diagonal band (or every tile when
+  // the key tile is ragged) run with the mask; the rest need none.
+  const int qt_mask_end = (kv0 + BC > N) ? n_qt : (CAUSAL ? min(n_qt, (kv0 + BC - 1) / BR + 1) : qt_begin);
+  int qt = qt_begin, it = 0;
+  for (; qt < qt_mask_end; ++qt, ++it) iteration(qt, it, BoolC<true>{});
+  for (; qt < n_qt; ++qt, ++it) iteration(qt, it, BoolC<false>{});
 
   if (kj < N) {
     T* dKj = dK + base + (size_t)kj * D;
@@ -369,14 +377,15 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   store_tile(0);
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto tile = [&](int kt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const bool more = kt + 1 < n_kt;
     if (more) load_tile(kt + 1);
     const T* ks = Ks[kt & 1];
     const T* vs = Vs[kt & 1];
     const int kb0 = kt * BC;
     const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
-    const int nlive = last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1);
+    const int nlive = MASKED ? (last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1)) : C::NJB;
 #pragma unroll
     for (int jb = 0; jb < C::NJB; ++jb) {
       if (jb < nlive) {
@@ -389,11 +398,10 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
           mfma_chunk<T>(dp, load16(vrow + c * 2 * CH), gf[c]);
         }
         const int kb = kb0 + 32 * jb;
-        const bool need_mask = (CAUSAL && kb + 31 > qw) || kb + 32 > N;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
-          if (need_mask) {
+          if (MASKED) {
             const int j = kb + acc_row(r, h);
             if ((CAUSAL && j > qi) || j >= N) p = 0.f;
           }
@@ -411,7 +419,13 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
     }
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
-  }
+  };
+  // Key tiles wholly below every row of this query tile and wholly before N
+  // need no mask; the diagonal and ragged tiles come last.
+  const int kt_full = min(n_kt, CAUSAL ? min(q0, N) / BC : N / BC);
+  int kt = 0;
+  for (; kt < kt_full; ++kt) tile(kt, BoolC<false>{});
+  for (; kt < n_kt; ++kt) tile(kt, BoolC<true>{});
 
   if (qi < N) {
     T* dQi = dQ + base + (size_t)qi * D;

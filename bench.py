@@ -46,10 +46,20 @@ def counted_flop(w):
     return fwd, 2.5 * fwd, 3.5 * fwd
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources; ties stored counter readings to a kernel version."""
+# Source files each kernel is compiled from (for tying stored counter
+# readings to the kernel version they were taken on).
+KERNEL_SOURCES = {
+    "fwd_kernel": ["fa2_fwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
+    "bwd_pre_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
+    "bwd_dkdv_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
+    "bwd_dq_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    """Hash of the HIP sources a kernel is built from."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -64,7 +74,7 @@ def stored_traffic(kernel: str, workload: str):
     text = open(path).read()
     m = re.search(r"source_hash:\s*([0-9a-f]+)", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not b or m.group(1) != source_hash():
+    if not m or not b or m.group(1) != source_hash(kernel):
         return None
     return float(b.group(1))
 
@@ -214,7 +224,7 @@ def main() -> int:
     for kk in ("fwd", "bwd"):
         detail[kk]["frac_peak"] = detail[kk]["tflops"] / peak
     detail["step_frac_peak"] = value / peak
-    detail["source_hash"] = source_hash()
+    detail["source_hash"] = {k: source_hash(k) for k in KERNEL_SOURCES}
     if args.cpu_budget > 0:
         cb, parity = cpu_baseline(w, (q, k, v, dO), (o, lse, dq, dk, dv), args.cpu_budget)
         result["cpu_baseline"] = cb

@@ -195,3 +195,19 @@ def test_rejects_bad_head_dim_on_gpu():
     q = torch.zeros((1, 1, 16, 48), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.Fa2Error):
         fa.forward(q, q, q)
+
+
+def test_lse_accuracy_bf16_tighter_than_tolerance():
+    """LSE comes from fp32 logits of bf16 inputs (exact products, fp32 sums),
+    so it should sit near fp32 rounding, far inside the 2e-2 bf16 limit.  A
+    tighter bound guards against shortcuts such as summing the bf16-rounded
+    weights (which moved LSE to ~1e-4)."""
+    for w in (workloads.custom(1, 4, 1000, 128, "bf16", True, 31, name="lse"),
+              workloads.custom(1, 4, 777, 64, "bf16", False, 32, qk_mult=8.0, name="lse")):
+        q, k, v, _ = workloads.make_inputs(w, device="cuda")
+        o, lse = fa.forward(q, k, v, w.causal, w.scale)
+        torch.cuda.synchronize()
+        _, lse_r = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), w.scale, w.causal)
+        err = rel_err(lse.cpu(), lse_r)
+        log("  %s LSE rel err %.3g" % (w.describe(), err))
+        assert err < 1e-5

@@ -199,6 +199,64 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   // A buffer is rewritten (store_q) one tile after its last reads, and every
   // wave has passed the barrier that follows those reads by then.
   const bool key_tail = kw + 31 >= N;  // this wave's keys reach past N
+  // One 32-query block of a step, in three parts: the S and dP products, the
+  // elementwise P = exp2(S*scale*log2e - LSE2), dS = P (dP - D) (rows past N
+  // have LSE2 = +inf, so P = 0), and the dV^T += dO^T P, dK^T += Q^T dS
+  // products, whose transposed operands are read straight from the
+  // row-major tiles.
+  auto mm_sdp = [&](const T* qs, const T* gs, int mb, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+    const T* qrow = qs + (32 * mb + l32) * QS + h * CH;
+    const T* grow = gs + (32 * mb + l32) * QS + h * CH;
+    // All operand fragments first, so the wave waits on LDS once per phase.
+    u32x4 qa[C::DCH], ga[C::DCH];
+#pragma unroll
+    for (int c = 0; c < C::DCH; ++c) {
+      qa[c] = load16(qrow + c * 2 * CH);
+      ga[c] = load16(grow + c * 2 * CH);
+    }
+#pragma unroll
+    for (int c = 0; c < C::DCH; ++c) {
+      mfma_chunk<T>(s, qa[c], kf[c]);
+      mfma_chunk<T>(dp, ga[c], vf[c]);
+    }
+  };
+  auto grad = [&](const float* ls, const float* ds, int i0, int mb, f32x16& s, f32x16& dp, auto masked) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int il = 32 * mb + 8 * g + 4 * h;  // rows il..il+3 of this lane
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + il);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + il);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * g + q;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
+        if (decltype(masked)::value && ((CAUSAL && kj > i0 + il + q) || kj >= N)) p = 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[q]);
+      }
+    }
+  };
+  auto mm_kv = [&](const T* qs, const T* gs, int mb, const f32x16& s, const f32x16& dp) {
+#pragma unroll
+    for (int t = 0; t < C::CPB; ++t) {
+      u32x4 ga[C::NB], qa[C::NB];
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b) {
+        ga[b] = load_rowcontract<T>(gs, QS, 32 * mb, t, 32 * b, C::CMASK, lane);
+        qa[b] = load_rowcontract<T>(qs, QS, 32 * mb, t, 32 * b, C::CMASK, lane);
+      }
+      const u32x4 pb = pack_chunk<T>(s, t);
+      const u32x4 sb = pack_chunk<T>(dp, t);
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b) {
+        mfma_chunk<T>(dv[b], ga[b], pb);
+        mfma_chunk<T>(dk[b], qa[b], sb);
+      }
+    }
+  };
+
   auto iteration = [&](int qt, int it, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     const int buf = it & 1;
@@ -208,47 +266,28 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     const float* ds = dl_s[buf];
     const int i0 = qt * BR;
 
+    if (MASKED || MB != 2 || sizeof(T) != 2) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int ib = i0 + 32 * mb;
-      if (kw < N && ib < N && (!CAUSAL || ib + 31 >= kw)) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const T* qrow = qs + (32 * mb + l32) * QS + h * CH;
-        const T* grow = gs + (32 * mb + l32) * QS + h * CH;
-#pragma unroll
-        for (int c = 0; c < C::DCH; ++c) {
-          mfma_chunk<T>(s, load16(qrow + c * 2 * CH), kf[c]);
-          mfma_chunk<T>(dp, load16(grow + c * 2 * CH), vf[c]);
-        }
-        // P = exp2(S*scale*log2e - LSE2) and dS = P (dP - D); rows past N
-        // have LSE2 = +inf and so P = 0.
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int il = 32 * mb + 8 * g + 4 * h;  // rows il..il+3 of this lane
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + il);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + il);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * g + q;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
-            if (MASKED && ((CAUSAL && kj > i0 + il + q) || kj >= N)) p = 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - d4[q]);
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (contraction over the query rows,
-        // the transposed operands read straight from the row-major tiles).
-#pragma unroll
-        for (int t = 0; t < C::CPB; ++t) {
-          const u32x4 pb = pack_chunk<T>(s, t);
-          const u32x4 sb = pack_chunk<T>(dp, t);
-#pragma unroll
-          for (int b = 0; b < C::NB; ++b) {
-            mfma_chunk<T>(dv[b], load_rowcontract<T>(gs, QS, 32 * mb, t, 32 * b, C::CMASK, lane), pb);
-            mfma_chunk<T>(dk[b], load_rowcontract<T>(qs, QS, 32 * mb, t, 32 * b, C::CMASK, lane), sb);
-          }
+      for (int mb = 0; mb < MB; ++mb) {
+        const int ib = i0 + 32 * mb;
+        if (kw < N && ib < N && (!CAUSAL || ib + 31 >= kw)) {
+          f32x16 s, dp;
+          mm_sdp(qs, gs, mb, s, dp);
+          grad(ls, ds, i0, mb, s, dp, masked);
+          mm_kv(qs, gs, mb, s, dp);
         }
       }
+    } else {
+      // Bulk step (every block live, no mask), ordered so the one wave per
+      // SIMD has independent MFMAs issued ahead of each block's VALU work.
+      // Blocks past N carry P = 0 (LSE2 = +inf) and need no test.
+      f32x16 s0, dp0, s1, dp1;
+      mm_sdp(qs, gs, 0, s0, dp0);
+      mm_sdp(qs, gs, 1, s1, dp1);
+      grad(ls, ds, i0, 0, s0, dp0, BoolC<false>{});
+      mm_kv(qs, gs, 0, s0, dp0);
+      grad(ls, ds, i0, 1, s1, dp1, BoolC<false>{});
+      mm_kv(qs, gs, 1, s1, dp1);
     }
     if (qt + 1 < n_qt) store_q(buf ^ 1);
     __syncthreads();

@@ -232,7 +232,8 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
       for (int q = 0; q < 4; ++q) {
         const int r = 4 * g + q;
         float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
-        if (decltype(masked)::value && ((CAUSAL && kj > i0 + il + q) || kj >= N)) p = 0.f;
+        if (decltype(masked)::value)  // bitwise, so it stays a select, not a branch
+          p = ((CAUSAL & (kj > i0 + il + q)) | (kj >= N)) ? 0.f : p;
         s[r] = p;
         dp[r] = p * (dp[r] - d4[q]);
       }
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
           float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
           if (MASKED) {
             const int j = kb + acc_row(r, h);
-            if ((CAUSAL && j > qi) || j >= N) p = 0.f;
+            p = ((CAUSAL & (j > qi)) | (j >= N)) ? 0.f : p;  // a select, not a branch
           }
           dp[r] = p * (dp[r] - dl);
         }
@@ -481,6 +482,271 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV for bf16 with d = 128: 8 waves as two groups that alternate query
+// steps over the same 128 keys, so every SIMD runs two waves (one per group)
+// and one wave's softmax work overlaps the other's MFMAs.  Register budget
+// (<= 256 per wave): K rows and the dK^T, dV^T partial accumulators stay in
+// registers; V rows come from LDS.  Q and dO tiles (32 rows per group step,
+// double-buffered) are filled by direct global->LDS loads into unpadded
+// 256-byte rows whose 16-byte chunks are XOR-swizzled (chunk c of row r at
+// c ^ swz(r)): 16 lanes reading one chunk of 16 consecutive rows, and the
+// 4-row x 32-byte windows of a transpose read, both land on distinct banks.
+// The two groups' partial dK, dV are summed through LDS at the end.
+// ---------------------------------------------------------------------------
+namespace pp {
+constexpr int D = 128;
+constexpr int ROWE = 128;  // elements per LDS row
+constexpr int BC = 128;    // keys per workgroup
+constexpr int BR = 32;     // query rows per group step
+constexpr int TILE_E = BR * ROWE;
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16*lane.
+__device__ __forceinline__ void dload16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+// 4 bytes per lane into LDS at lds + 4*lane.
+__device__ __forceinline__ void dload4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte offsets inside a swizzled tile.  The swizzle only touches bits 4..7
+// of a row's byte offset, so every fragment offset a lane needs is one of a
+// few per-lane values XORed with a compile-time constant.
+//   Row fragment (lane row l32, chunk 2c + h):  rofs ^ (c << 5)
+//   Transpose fragment (t, column block b), the two 4-row halves:
+//     t*4096 + tofs0 + ((b ^ kk) << 6)  and  t*4096 + tofs1 + ((b ^ kk) << 6)
+struct SwzOffsets {
+  int rofs, tofs0, tofs1, kk;
+};
+__device__ __forceinline__ SwzOffsets swz_offsets(int lane) {
+  const int l32 = lane & 31, h = lane >> 5, j = lane & 15;
+  SwzOffsets o;
+  o.rofs = l32 * 256 + ((h ^ swz(l32)) << 4);
+  const int r0 = 4 * h + (j >> 2);  // < 8, so swz(r0 + 8) = swz(r0) ^ 1
+  const int s0 = swz(r0);
+  const int c1 = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+  o.tofs0 = r0 * 256 + ((c1 ^ (s0 & 3)) << 4) + 8 * (j & 1);
+  o.tofs1 = (r0 + 8) * 256 + ((c1 ^ ((s0 ^ 1) & 3)) << 4) + 8 * (j & 1);
+  o.kk = s0 >> 2;
+  return o;
+}
+__device__ __forceinline__ u32x4 lds16(const void* base, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+// Transposed fragment (see load_rowcontract) from two byte offsets.
+__device__ __forceinline__ u32x4 tr_frag(const void* base, int off0, int off1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const char* b = reinterpret_cast<const char*>(base);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + off0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + off1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+}  // namespace pp
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __restrict__ Q,
+                                                              const __bf16* __restrict__ K,
+                                                              const __bf16* __restrict__ V,
+                                                              const __bf16* __restrict__ dO,
+                                                              const float* __restrict__ LSE,
+                                                              const float* __restrict__ Delta,
+                                                              __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                                                              int N, int BH, float sl2, float scale) {
+  using namespace pp;
+  typedef __bf16 T;
+  constexpr int CH = 8, DCH = D / 16, NB = D / 32;
+  __shared__ __attribute__((aligned(16))) T Vs[BC * ROWE];             // 32 KB
+  __shared__ __attribute__((aligned(16))) T QdO[2][2][2][TILE_E];      // [buf][group][Q|dO], 64 KB
+  __shared__ __attribute__((aligned(16))) float LD[2][2][64];          // [buf][group][LSE 32 | D 32]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int grp = w >> 2, kb = w & 3;
+  const int lin = blockIdx.x;
+  const int kt = lin / BH;  // ascending: for causal the heaviest key tiles go first
+  const int bh = lin % BH;
+  const size_t base = (size_t)bh * N * D;
+  const T* Qh = Q + base;
+  const T* dOh = dO + base;
+  const T* Vh = V + base;
+  const float* lseh = LSE + (size_t)bh * N;
+  const float* dlh = Delta + (size_t)bh * N;
+  const int kv0 = kt * BC;
+  const int kw = kv0 + 32 * kb;  // first key of this wave
+  const int kj = kw + l32;       // key owned by this lane
+
+  u32x4 kf[DCH];
+  {
+    const T* krow = K + base + (size_t)min(kj, N - 1) * D + h * CH;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) kf[c] = load16(krow + c * 2 * CH);
+  }
+  f32x16 dk[NB], dv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    dk[b] = f32x16{};
+    dv[b] = f32x16{};
+  }
+
+  const int n_qt = (N + BR - 1) / BR;
+  const int qt_begin = CAUSAL ? kv0 / BR : 0;
+  const int n_ds = (n_qt - qt_begin + 1) / 2;  // double steps (one step per group)
+
+  // V tile: 32 one-kilobyte loads, 4 per wave (rows past N read row N-1).
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = 4 * w + u;
+    const int r = 4 * k + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    dload16(Vh + (size_t)min(kv0 + r, N - 1) * D + c * 8, &Vs[k * 512]);
+  }
+  // Q, dO, LSE, D of double step ds into buffer buf: 2 groups x 2 tensors x
+  // 8 loads, 4 per wave; wave 0 / wave 4 fetch LSE and D of group 0 / 1.
+  auto issue = [&](int ds, int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = 4 * w + u;
+      const int g = q >> 4, tens = (q >> 3) & 1, k = q & 7;
+      const int step = qt_begin + 2 * ds + g;
+      if (step < n_qt) {
+        const int r = 4 * k + (lane >> 4);
+        const int c = (lane & 15) ^ swz(r);
+        const T* src = (tens ? dOh : Qh) + (size_t)min(step * BR + r, N - 1) * D + c * 8;
+        dload16(src, &QdO[buf][g][tens][k * 512]);
+      }
+    }
+    if (kb == 0) {
+      const int step = qt_begin + 2 * ds + grp;
+      if (step < n_qt) {
+        const int i = min(step * BR + l32, N - 1);
+        dload4(h ? dlh + i : lseh + i, &LD[buf][grp][0]);
+      }
+    }
+  };
+
+  if (n_ds > 0) issue(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  const SwzOffsets so = swz_offsets(lane);
+  // One group step: 32 query rows against this wave's 32 keys.
+  auto step_body = [&](const T* qt, const T* gt, const float* ld, int i0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // Launder the lane offsets so the per-fragment XORs are recomputed each
+    // step instead of being hoisted into dozens of live registers.
+    int rofs = so.rofs, tofs0 = so.tofs0, tofs1 = so.tofs1, kk = so.kk;
+    asm volatile("" : "+v"(rofs), "+v"(tofs0), "+v"(tofs1), "+v"(kk));
+    const char* vrow = reinterpret_cast<const char*>(Vs) + kb * 32 * 256;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      const int ro = rofs ^ (c << 5);
+      mfma_chunk<T>(s, lds16(qt, ro), kf[c]);
+      mfma_chunk<T>(dp, lds16(gt, ro), lds16(vrow, ro));
+    }
+    // Row of accumulator r is i0 + 4h + (8*(r/4) + r%4); the mask compares
+    // two per-lane thresholds against that compile-time constant.
+    const int t_causal = kj - i0 - 4 * h;  // masked when t_causal > c_r
+    const int t_rows = N - i0 - 4 * h;     // masked when c_r >= t_rows
+    const bool key_dead = kj >= N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int il = 8 * g + 4 * h;  // rows il..il+3 of this lane
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ld + il);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ld + 32 + il);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * g + q;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q] * kLog2e));
+        if (MASKED) {
+          const int c_r = 8 * g + q;
+          p = ((CAUSAL & (t_causal > c_r)) | (c_r >= t_rows) | key_dead) ? 0.f : p;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[q]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pb = pack_chunk<T>(s, t);
+      const u32x4 sb = pack_chunk<T>(dp, t);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int cb = ((b ^ kk) << 6) + t * 4096;
+        mfma_chunk<T>(dv[b], tr_frag(gt, tofs0 + cb, tofs1 + cb), pb);
+        mfma_chunk<T>(dk[b], tr_frag(qt, tofs0 + cb, tofs1 + cb), sb);
+      }
+    }
+  };
+
+  auto double_step = [&](int ds, auto masked) {
+    const int buf = ds & 1;
+    if (ds + 1 < n_ds) issue(ds + 1, buf ^ 1);
+    const int step = qt_begin + 2 * ds + grp;
+    if (step < n_qt) {
+      const int i0 = step * BR;
+      // Skip blocks with no visible key (all above the diagonal, or keys
+      // past N); they would only add zeros.
+      if (!decltype(masked)::value || (kw < N && (!CAUSAL || i0 + 31 >= kw)))
+        step_body(QdO[buf][grp][0], QdO[buf][grp][1], LD[buf][grp], i0, masked);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  // Double steps whose two query steps are both off the diagonal band, both
+  // complete (32 rows < N) and on a complete key tile need no mask; only a
+  // prefix (the diagonal) and a suffix (the ragged end) do.
+  const int full_steps = N / BR - qt_begin;
+  const int ds_bulk_begin = (kv0 + BC > N) ? n_ds : (CAUSAL ? min(n_ds, 2) : 0);
+  const int ds_bulk_end = max(ds_bulk_begin, min(n_ds, full_steps / 2));
+  int ds = 0;
+  for (; ds < ds_bulk_begin; ++ds) double_step(ds, BoolC<true>{});
+  for (; ds < ds_bulk_end; ++ds) double_step(ds, BoolC<false>{});
+  for (; ds < n_ds; ++ds) double_step(ds, BoolC<true>{});
+
+  // Sum the two groups' partial accumulators through LDS (reusing QdO).
+  float* red = reinterpret_cast<float*>(&QdO[0][0][0][0]);  // 16384 floats
+  auto reduce = [&](f32x16 (&acc)[NB]) {
+    if (grp == 1) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((kb * NB + b) * 16 + r) * 64 + lane] = acc[b][r];
+    }
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] += red[((kb * NB + b) * 16 + r) * 64 + lane];
+    }
+    __syncthreads();
+  };
+  reduce(dk);
+  reduce(dv);
+
+  if (grp == 0 && kj < N) {
+    T* dKj = dK + base + (size_t)kj * D;
+    T* dVj = dV + base + (size_t)kj * D;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * b + 8 * g + 4 * h;
+        store4<T>(dKj + d0, dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale, dk[b][4 * g + 2] * scale,
+                  dk[b][4 * g + 3] * scale);
+        store4<T>(dVj + d0, dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2], dv[b][4 * g + 3]);
+      }
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
@@ -490,6 +756,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     constexpr int RPB = 256 / (D / Elt<T>::CH);
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.delta, rows);
+    return hipGetLastError();
+  }
+  if (stage == 2 && sizeof(T) == 2 && D == 128) {
+    const long long blocks = (long long)((a.N + pp::BC - 1) / pp::BC) * BH;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dkdv_pp_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(512), 0, a.stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse, a.delta,
+                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, sl2, a.scale);
     return hipGetLastError();
   }
   if (stage == 2) {

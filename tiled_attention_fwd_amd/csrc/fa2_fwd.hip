@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int j = kb + acc_row(r, h);
-              if ((CAUSAL && j > qi) || j >= N) s[jb][r] = -INFINITY;
+              s[jb][r] = ((CAUSAL & (j > qi)) | (j >= N)) ? -INFINITY : s[jb][r];  // a select
             }
           }
 #pragma unroll

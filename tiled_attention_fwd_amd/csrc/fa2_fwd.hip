@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   store_tile(0);
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // One key tile.  Each 32-key block runs its own online-softmax update, so
+  // a block's exponentials depend only on its own scores and the next
+  // block's score MFMAs can run under them.
+  auto tile = [&](int kt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const bool more = kt + 1 < n_kt;
     if (more) load_tile(kt + 1);
     const T* ks = Ks[kt & 1];
@@ -137,74 +141,72 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     const int kb0 = kt * BC;
     // 32-key blocks of this tile that hold a key this wave may see.
     const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
-    const int nlive = last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1);
+    const int nlive = MASKED ? (last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1)) : C::NJB;
 
-    if (nlive > 0) {
-      f32x16 s[C::NJB];
+    f32x16 s[C::NJB];
 #pragma unroll
-      for (int jb = 0; jb < C::NJB; ++jb) {
-        if (jb < nlive) {
-          s[jb] = f32x16{};
-          const T* krow = ks + (32 * jb + l32) * KS + h * CH;
+    for (int jb = 0; jb < C::NJB; ++jb) {
+      if (jb < nlive) {
+        s[jb] = f32x16{};
+        const T* krow = ks + (32 * jb + l32) * KS + h * CH;
 #pragma unroll
-          for (int c = 0; c < C::DCH; ++c) mfma_chunk<T>(s[jb], load16(krow + c * 2 * CH), qf[c]);
-        }
+        for (int c = 0; c < C::DCH; ++c) mfma_chunk<T>(s[jb], load16(krow + c * 2 * CH), qf[c]);
       }
-      float mx = -INFINITY;
+    }
 #pragma unroll
-      for (int jb = 0; jb < C::NJB; ++jb) {
-        if (jb < nlive) {
-          const int kb = kb0 + 32 * jb;
-          if ((CAUSAL && kb + 31 > qw) || kb + 32 > N) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = kb + acc_row(r, h);
-              s[jb][r] = ((CAUSAL & (j > qi)) | (j >= N)) ? -INFINITY : s[jb][r];  // a select
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[jb][r], s[jb][r + 1]));
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_cand = mx * sl2;
-      const bool grow = m_cand > m_run + kSlack;
-      if (__any(grow)) {
-        const float m_new = grow ? m_cand : m_run;
-        // 0 on a lane's first visible keys; exactly 1 where the max stays.
-        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < C::NB; ++b) o[b] *= alpha;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-
-#pragma unroll
-      for (int jb = 0; jb < C::NJB; ++jb) {
-        if (jb < nlive) {
-          // The row sum is taken over the fp32 weights (summing the rounded
-          // bf16 weights instead costs LSE accuracy: ~1e-4 relative).
-          float l_blk = 0.f;
+    for (int jb = 0; jb < C::NJB; ++jb) {
+      if (jb < nlive) {
+        const int kb = kb0 + 32 * jb;
+        if (MASKED) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            s[jb][r] = __builtin_amdgcn_exp2f(fmaf(s[jb][r], sl2, neg_m));
-            l_blk += s[jb][r];
+            const int j = kb + acc_row(r, h);
+            s[jb][r] = ((CAUSAL & (j > qi)) | (j >= N)) ? -INFINITY : s[jb][r];  // a select
           }
-          l_run += l_blk;
+        }
+        float mx = s[jb][0];
 #pragma unroll
-          for (int t = 0; t < C::CPB; ++t) {
-            const u32x4 pb = pack_chunk<T>(s[jb], t);
+        for (int r = 1; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[jb][r], s[jb][r + 1 < 16 ? r + 1 : r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_cand = mx * sl2;
+        const bool grow = m_cand > m_run + kSlack;
+        if (__any(grow)) {
+          const float m_new = grow ? m_cand : m_run;
+          // 0 on a lane's first visible keys; exactly 1 where the max stays.
+          const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-            for (int b = 0; b < C::NB; ++b)
-              mfma_chunk<T>(o[b], load_rowcontract<T>(vs, VS, 32 * jb, t, 32 * b, C::CMASK, lane), pb);
-          }
+          for (int b = 0; b < C::NB; ++b) o[b] *= alpha;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        // The row sum is taken over the fp32 weights (summing the rounded
+        // bf16 weights instead costs LSE accuracy: ~1e-4 relative).
+        float l_blk = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[jb][r] = __builtin_amdgcn_exp2f(fmaf(s[jb][r], sl2, neg_m));
+          l_blk += s[jb][r];
+        }
+        l_run += l_blk;
+#pragma unroll
+        for (int t = 0; t < C::CPB; ++t) {
+          const u32x4 pb = pack_chunk<T>(s[jb], t);
+#pragma unroll
+          for (int b = 0; b < C::NB; ++b)
+            mfma_chunk<T>(o[b], load_rowcontract<T>(vs, VS, 32 * jb, t, 32 * b, C::CMASK, lane), pb);
         }
       }
     }
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
-  }
+  };
+  // Key tiles wholly below every row of this query tile and wholly before N
+  // need no mask; the diagonal and ragged tiles come last.
+  const int kt_full = min(n_kt, CAUSAL ? min(q0, N) / BC : N / BC);
+  int kt = 0;
+  for (; kt < kt_full; ++kt) tile(kt, BoolC<false>{});
+  for (; kt < n_kt; ++kt) tile(kt, BoolC<true>{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qi < N) {

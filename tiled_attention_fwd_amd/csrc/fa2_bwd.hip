@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float lse_s[2][BR];
   __shared__ __attribute__((aligned(16))) float dl_s[2][BR];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
   const int kt = lin / BH;  // ascending: for causal the heaviest key tiles go first
@@ -355,7 +356,8 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
   __shared__ __attribute__((aligned(16))) T Vs[2][BC * VS];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
@@ -504,15 +506,47 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16*lane.
-__device__ __forceinline__ void dload16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+// Direct global-to-LDS loads.  They are issued from inline assembly so that
+// the compiler does not see them as LDS writes: it would otherwise make the
+// first LDS read after each one wait for it, whatever buffer it reads.  The
+// kernels therefore order them by hand: wait_vmem() and a barrier before any
+// read of the data they bring.
+// M0 is named as clobbered; clang notes that it is a reserved register, which
+// is what is wanted here (nothing keeps a value in M0 across these).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ unsigned lds_off(const void* p) { return (unsigned)(size_t)(const lds_void*)p; }
+// 16 bytes per lane from 64-bit global address g into LDS at lds + 16*lane
+// (lds wave-uniform).
+__device__ __forceinline__ void dload16(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_off(lds)) : "memory", "m0");
 }
 // 4 bytes per lane into LDS at lds + 4*lane.
-__device__ __forceinline__ void dload4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+__device__ __forceinline__ void dload4(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_off(lds)) : "memory", "m0");
 }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Raw buffer resource over `bytes` bytes at `base` (stride 0, gfx9 data
+// format 32); base must be wave-uniform.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
+  const size_t a = (size_t)base;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r.y = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;
+  return r;
+}
+// 16 bytes per lane from buffer offset voffset + soffset into LDS at
+// lds + 16*lane (soffset and lds wave-uniform).
+__device__ __forceinline__ void bload16(u32x4 r, int voffset, int soffset, const void* lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voffset), "s"(r),
+               "s"(lds_off(lds)), "s"(soffset)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima) through the builtin,
+// so that the compiler's own wait tracking sees it.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Byte offsets inside a swizzled tile.  The swizzle only touches bits 4..7
 // of a row's byte offset, so every fragment offset a lane needs is one of a
@@ -565,7 +599,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
   __shared__ __attribute__((aligned(16))) T QdO[2][2][2][TILE_E];      // [buf][group][Q|dO], 64 KB
   __shared__ __attribute__((aligned(16))) float LD[2][2][64];          // [buf][group][LSE 32 | D 32]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int grp = w >> 2, kb = w & 3;
   const int lin = blockIdx.x;
@@ -580,6 +615,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
   const int kv0 = kt * BC;
   const int kw = kv0 + 32 * kb;  // first key of this wave
   const int kj = kw + l32;       // key owned by this lane
+  const u32x4 rq = make_rsrc(Qh, (unsigned)N * D * 2);
+  const u32x4 rdo = make_rsrc(dOh, (unsigned)N * D * 2);
 
   u32x4 kf[DCH];
   {
@@ -608,6 +645,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
   }
   // Q, dO, LSE, D of double step ds into buffer buf: 2 groups x 2 tensors x
   // 8 loads, 4 per wave; wave 0 / wave 4 fetch LSE and D of group 0 / 1.
+  // Complete 32-row steps take the row offset as the uniform buffer offset;
+  // a ragged last step clamps its rows to N-1 per lane.
   auto issue = [&](int ds, int buf) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -616,9 +655,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
       const int step = qt_begin + 2 * ds + g;
       if (step < n_qt) {
         const int r = 4 * k + (lane >> 4);
-        const int c = (lane & 15) ^ swz(r);
-        const T* src = (tens ? dOh : Qh) + (size_t)min(step * BR + r, N - 1) * D + c * 8;
-        dload16(src, &QdO[buf][g][tens][k * 512]);
+        const int col = ((lane & 15) ^ swz(r)) * 16;
+        const u32x4 rs = tens ? rdo : rq;
+        if ((step + 1) * BR <= N)
+          bload16(rs, r * 256 + col, step * BR * 256, &QdO[buf][g][tens][k * 512]);
+        else
+          bload16(rs, min(step * BR + r, N - 1) * 256 + col, 0, &QdO[buf][g][tens][k * 512]);
       }
     }
     if (kb == 0) {

@@ -502,7 +502,13 @@ constexpr int ROWE = 128;  // elements per LDS row
 constexpr int BC = 128;    // keys per workgroup
 constexpr int BR = 32;     // query rows per group step
 constexpr int TILE_E = BR * ROWE;
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Tiles are stored unpadded, 256 bytes per row, with the sixteen 16-byte
+// chunks of row r permuted as chunk ^ swz(r).  swz is a permutation over any
+// 16 consecutive rows, so the 16 lanes that read one chunk of 16 rows hit
+// all 64 banks once; and rows r..r+3 (r % 4 == 0) move a 64-byte column
+// block to four different 64-byte positions, so a transposed read, whose 32
+// lanes take one column block from 4 rows, also covers every bank once.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -561,11 +567,11 @@ __device__ __forceinline__ SwzOffsets swz_offsets(int lane) {
   const int l32 = lane & 31, h = lane >> 5, j = lane & 15;
   SwzOffsets o;
   o.rofs = l32 * 256 + ((h ^ swz(l32)) << 4);
-  const int r0 = 4 * h + (j >> 2);  // < 8, so swz(r0 + 8) = swz(r0) ^ 1
+  const int r0 = 4 * h + (j >> 2);  // < 8, so swz(r0 + 8) = swz(r0) ^ 2
   const int s0 = swz(r0);
   const int c1 = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
   o.tofs0 = r0 * 256 + ((c1 ^ (s0 & 3)) << 4) + 8 * (j & 1);
-  o.tofs1 = (r0 + 8) * 256 + ((c1 ^ ((s0 ^ 1) & 3)) << 4) + 8 * (j & 1);
+  o.tofs1 = (r0 + 8) * 256 + ((c1 ^ ((s0 & 3) ^ 2)) << 4) + 8 * (j & 1);
   o.kk = s0 >> 2;
   return o;
 }
@@ -686,12 +692,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
     asm volatile("" : "+v"(rofs), "+v"(tofs0), "+v"(tofs1), "+v"(kk));
     const char* vrow = reinterpret_cast<const char*>(Vs) + kb * 32 * 256;
     f32x16 s = f32x16{}, dp = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
       const int ro = rofs ^ (c << 5);
       mfma_chunk<T>(s, lds16(qt, ro), kf[c]);
       mfma_chunk<T>(dp, lds16(gt, ro), lds16(vrow, ro));
     }
+    // reads of chunk c+1 (3) issued before the two products of chunk c
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int c = 0; c < DCH - 2; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // Row of accumulator r is i0 + 4h + (8*(r/4) + r%4); the mask compares
     // two per-lane thresholds against that compile-time constant.
     const int t_causal = kj - i0 - 4 * h;  // masked when t_causal > c_r
@@ -714,6 +730,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
         dp[r] = p * (dp[r] - d4[q]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u32x4 pb = pack_chunk<T>(s, t);
@@ -725,6 +742,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
         mfma_chunk<T>(dk[b], tr_frag(qt, tofs0 + cb, tofs1 + cb), sb);
       }
     }
+    // fragments two products ahead: 4 reads, then (product, 2 reads) x 14, 2 products
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 13; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   auto double_step = [&](int ds, auto masked) {
@@ -773,18 +799,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
   reduce(dk);
   reduce(dv);
 
-  if (grp == 0 && kj < N) {
-    T* dKj = dK + base + (size_t)kj * D;
-    T* dVj = dV + base + (size_t)kj * D;
+  // Stage the bf16 results row-major in LDS (16-byte chunks swizzled like
+  // the tiles): dK in the V tile, dV in the first 32 KB of the Q/dO buffers,
+  // both free now.  Then all eight waves store whole 256-byte rows.
+  T* sk = Vs;
+  T* sv = &QdO[0][0][0][0];
+  if (grp == 0) {
+    const int row = 32 * kb + l32;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * b + 8 * g + 4 * h;
-        store4<T>(dKj + d0, dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale, dk[b][4 * g + 2] * scale,
+        const int off = row * ROWE + (((4 * b + g) ^ swz(row)) << 3) + 4 * h;
+        store4<T>(sk + off, dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale, dk[b][4 * g + 2] * scale,
                   dk[b][4 * g + 3] * scale);
-        store4<T>(dVj + d0, dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2], dv[b][4 * g + 3]);
+        store4<T>(sv + off, dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2], dv[b][4 * g + 3]);
       }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * w + 4 * i + (lane >> 4);
+    const int ch = lane & 15;
+    const int key = kv0 + row;
+    if (key < N) {
+      const int off = (row * ROWE + ((ch ^ swz(row)) << 3)) * 2;
+      store16(dK + base + (size_t)key * D + ch * 8, lds16(sk, off));
+      store16(dV + base + (size_t)key * D + ch * 8, lds16(sv, off));
     }
   }
 }

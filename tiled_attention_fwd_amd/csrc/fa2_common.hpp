@@ -196,6 +196,34 @@ __device__ __forceinline__ void write_transposed4<__bf16>(__bf16* tile, int row_
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// The value held by lane l ^ 32 (the other half of the wave), through the
+// gfx950 half-swap of two registers: a VALU operation, where a shuffle would
+// make a round trip through the LDS unit.  The swap exchanges the upper half
+// of its first operand with the lower half of its second, so with both set
+// to v the lower lanes find the partner's value in the second result and the
+// upper lanes in the first.
+__device__ __forceinline__ float swap_halves(float v, int lane) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+}
+
+// Row stride (in 4-byte words) for an LDS tile that is only read through
+// transpose reads.  The 32 lanes that the LDS serves together take a 64-byte
+// column block (16 banks) from each of 4 consecutive rows, so the row starts
+// stride*k mod 64 (k = 1..3) must keep those 16-bank windows apart.  Returns
+// the smallest stride >= row_words that does.
+constexpr int tr_stride_words(int row_words) {
+  for (int s = row_words;; ++s) {
+    bool ok = true;
+    for (int k = 1; k < 4 && ok; ++k) {
+      const int d = (s * k) % 64;
+      if (d < 16 || d > 48) ok = false;
+    }
+    if (ok) return s;
+  }
+}
+
 // Row stride (in 4-byte words) for an LDS tile whose rows hold `row_words`
 // words and that is read both ways: 16 lanes reading 16 B from 16
 // consecutive rows (row-contiguous MFMA operands) need (stride/4) odd, so the

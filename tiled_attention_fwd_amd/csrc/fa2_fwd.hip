@@ -13,7 +13,7 @@
 // computes the TRANSPOSED score block S^T = K Q^T (keys x queries) on MFMA,
 // so every lane owns one query column: its running max m and sum l are
 // plain per-lane registers, the row reduction is a loop over the lane's own
-// accumulators plus one exchange with lane l^32, and the exponentiated block
+// accumulators plus one half-swap with lane l^32, and the exponentiated block
 // is already laid out as the B operand of O^T += V^T P^T.  K and V tiles are
 // staged row-major in LDS (global loads of tile j+1 are issued before tile j
 // is computed and land in the other buffer; one barrier per tile).  The V^T
@@ -45,9 +45,10 @@ struct FwdTile {
   static constexpr int BC = sizeof(T) == 2 ? 64 : 32;  // keys per LDS tile
   static constexpr int CH = Elt<T>::CH;
   static constexpr int KS = D + CH;  // K row stride: 16-byte pad, conflict-free row reads
-  // V row stride: bf16 transpose reads touch 4 consecutive rows per 16 lanes;
-  // a 32-byte pad puts those rows on disjoint banks.
-  static constexpr int VS = sizeof(T) == 2 ? D + 16 : D + 4;
+  // V row stride: V is only read through transpose reads (bf16), which need
+  // 4 consecutive rows on disjoint 16-bank windows (and at least 32 columns
+  // per row, which is what a read spans); fp32 reads 4 rows per lane.
+  static constexpr int VS = sizeof(T) == 2 ? 2 * tr_stride_words((D >= 32 ? D : 32) / 2) : D + 4;
   static constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-row output blocks over d
   static constexpr int CMASK = (D >= 32 ? 32 : D) - 1;
   static constexpr int DCH = D / (2 * CH);  // chunks of a contraction over d
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
         float mx = s[jb][0];
 #pragma unroll
         for (int r = 1; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[jb][r], s[jb][r + 1 < 16 ? r + 1 : r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, swap_halves(mx, lane));
         const float m_cand = mx * sl2;
         const bool grow = m_cand > m_run + kSlack;
         if (__any(grow)) {
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   for (; kt < kt_full; ++kt) tile(kt, BoolC<false>{});
   for (; kt < n_kt; ++kt) tile(kt, BoolC<true>{});
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + swap_halves(l_run, lane);
   if (qi < N) {
     const float inv = 1.0f / l_tot;
     T* Oi = O + base + (size_t)qi * D;

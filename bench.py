@@ -3,9 +3,10 @@
 
 One step = the whole hot path over one batch of the large causal bf16
 workload (B=4, H=16, N=4096, d=128): ``fa2_forward`` and then the three
-backward stages (D preprocessing, the key-tile kernel, dQ conversion),
+backward stages (D = rowsum(dO * O), the dK/dV kernel, the dQ kernel),
 i.e. exactly ``fa2_backward``, called stage by stage so that HIP events on
-the launch stream can time each kernel.  Inputs are seeded synthetic tensors
+the launch stream can time each kernel.  The default 30 warmup steps let
+the clocks settle; 100 timed steps take about 0.15 s.  Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.
 
 Counted FLOP (causal halves it): forward 4*B*H*N^2*d/2, backward 2.5x that
@@ -120,8 +121,8 @@ def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0: skip)")

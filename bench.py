@@ -50,10 +50,10 @@ def counted_flop(w):
 # Source files each kernel is compiled from (for tying stored counter
 # readings to the kernel version they were taken on).
 KERNEL_SOURCES = {
-    "fwd_kernel": ["fa2_fwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
-    "bwd_pre_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
-    "bwd_dkdv_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
-    "bwd_dq_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp"],
+    "fwd_kernel": ["fa2_fwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
+    "bwd_pre_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
+    "bwd_dkdv_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
+    "bwd_dq_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
 }
 
 

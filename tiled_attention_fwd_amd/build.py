@@ -34,6 +34,10 @@ def compile_flags() -> list:
         "-munsafe-fp-atomics",
         # packed fp32 VALU forms stay off: the compiler must not emit them.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # No NaN ever reaches the kernels' arithmetic (masked scores are -inf,
+        # which this keeps): without it every fmaxf on an MFMA result first
+        # canonicalises its inputs, one extra VALU op per element.
+        "-fno-honor-nans",
         "-I", INCLUDE, "-I", CSRC,
         "-Wno-unused-command-line-argument",
     ]

@@ -9,6 +9,9 @@
 // softmax reduction is built up block by block.  What follows is that pass
 // laid out for CDNA4.
 //
+// Two kernels follow: fwd_kernel for every type and head size, and
+// fwd_pp_kernel, a leaner schedule of the same pass for bf16 and d = 128.
+//
 // Workgroup: 4 waves x 32 query rows = a 128-row query tile.  Each wave
 // computes the TRANSPOSED score block S^T = K Q^T (keys x queries) on MFMA,
 // so every lane owns one query column: its running max m and sum l are
@@ -33,6 +36,7 @@
 // fp32 and bf16.  At the end O = acc / l and LSE = (m + log2 l) * ln 2.
 #include "fa2_common.hpp"
 #include "fa2_launch.hpp"
+#include "fa2_swz.hpp"
 
 namespace fa2 {
 
@@ -227,8 +231,236 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   }
 }
 
+// Forward for bf16 and d = 128.  Same pass as fwd_kernel, organised around
+// 32-key blocks that reach LDS through direct loads into a ring of 4 block
+// slots (K and V, unpadded swizzled rows), issued 3 blocks ahead, one
+// barrier per block.  Within a wave the score products of block b+1 are
+// issued before the softmax of block b, so the matrix cores have work while
+// the exponentials of block b run; then P V of block b follows.
+//
+// On gfx950 a wave64 fp32 FMA occupies its SIMD for 4 clocks, an exp for 8
+// and a 32x32x16 MFMA for 32, and vector work only partly hides under the
+// products of the same or a neighbouring wave.  So the per-block vector
+// instruction count is what bounds this kernel next to the products, and it
+// is kept near the softmax's own work: lane offsets for every LDS fragment
+// and direct load are computed once, block slots are compile-time (the
+// block loop is unrolled over the ring), the row offset of a load goes in
+// the uniform buffer offset, and the rare running-max rescale is a real
+// branch.
+namespace fpp {
+constexpr int D = 128;
+constexpr int ROWE = 128;
+constexpr int BR = 128;        // query rows per workgroup (4 waves x 32)
+constexpr int KB = 32;         // keys per block
+constexpr int BLK_E = KB * ROWE;
+}  // namespace fpp
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                                                        float* __restrict__ LSE, int N, int BH, int num_qt,
+                                                        float sl2) {
+  using namespace tiles;
+  typedef __bf16 T;
+  constexpr int D = fpp::D, KB = fpp::KB, BLK_E = fpp::BLK_E;
+  constexpr int CH = 8, DCH = D / 16, NB = D / 32;
+  constexpr int R = 4, PF = R - 1;  // ring slots, blocks loaded ahead
+  __shared__ __attribute__((aligned(16))) T Ks[R][BLK_E];
+  __shared__ __attribute__((aligned(16))) T Vs[R][BLK_E];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int lin = blockIdx.x;
+  const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
+  const int bh = lin % BH;
+  const size_t base = (size_t)bh * N * D;
+  const T* Qh = Q + base;
+  const int q0 = qt * fpp::BR;
+  const int qw = q0 + 32 * w;  // first query row of this wave
+  const int qi = qw + l32;     // query row (column of S^T) owned by this lane
+  // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
+  // q = 4w + u, rows 4(q%8)..+3 of the block.
+  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + base, (unsigned)N * D * 2);
+  T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
+
+  const int kv_end = CAUSAL ? min(N, q0 + fpp::BR) : N;
+  const int nb = (kv_end + KB - 1) / KB;
+
+  // Per-lane constants: direct-load offsets within a block, and the LDS
+  // fragment offsets (K row fragments by chunk, V transpose fragments by
+  // column block and half); block slots and the t half are immediates.
+  int voff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
+    voff[u] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+  }
+  const SwzOffsets so = swz_offsets(lane);
+  int kofs[DCH], vofs0[NB], vofs1[NB];
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) kofs[c] = so.rofs ^ (c << 5);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    vofs0[b] = so.tofs0 + ((b ^ so.kk) << 6);
+    vofs1[b] = so.tofs1 + ((b ^ so.kk) << 6);
+  }
+
+  // Block kb into slot (its rows past N read row N-1; they are masked).
+  auto issue = [&](int kb, int slot) {
+    const int row0 = kb * KB;
+    T* dst = dst0 + slot * BLK_E;
+    if (row0 + KB <= N) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bload16(rsrc, voff[u], row0 * 256, dst + ((4 * w + u) & 7) * 512);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
+        bload16(rsrc, min(row0 + r, N - 1) * 256 + (voff[u] & 255), 0, dst + ((4 * w + u) & 7) * 512);
+      }
+    }
+  };
+
+  u32x4 qf[DCH];
+  {
+    const T* qrow = Qh + (size_t)min(qi, N - 1) * D + h * CH;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
+  }
+#pragma unroll
+  for (int b = 0; b < PF; ++b)
+    if (b < nb) issue(b, b);
+  wait_vmem();
+  __syncthreads();
+
+  // S^T = K Q^T for the block in slot (keys x this wave's 32 queries).
+  auto scores = [&](int slot) {
+    f32x16 s = f32x16{};
+    const char* kb_ = reinterpret_cast<const char*>(Ks[slot]);
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) mfma_chunk<T>(s, lds16(kb_, kofs[c]), qf[c]);
+    return s;
+  };
+
+  f32x16 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) o[b] = f32x16{};
+  float m_run = -INFINITY;  // running max of scaled logits, base-2 units
+  float l_run = 0.f;        // this lane half's share of the running sum
+
+  // Block kb (slot SLOT): scores of block kb+1 into s_nx, softmax and P V
+  // of block kb from s.
+  auto block = [&](auto slotc, int kb, auto masked, f32x16& s, f32x16& s_nx) {
+    constexpr int SLOT = decltype(slotc)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    const bool ahead = kb + PF < nb;
+    if (ahead) issue(kb + PF, (SLOT + PF) % R);
+    const int k0 = kb * KB;
+    if (MASKED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = k0 + acc_row(r, h);
+        s[r] = ((CAUSAL & (j > qi)) | (j >= N)) ? -INFINITY : s[r];
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1 < 16 ? r + 1 : r]));
+    mx = fmaxf(mx, swap_halves(mx, lane));
+    const float m_cand = mx * sl2;
+    const bool grow = m_cand > m_run + kSlack;
+    if (__builtin_expect(__any(grow), 0)) {
+      // Rare (the max moves by more than kSlack): kept as a real branch; the
+      // empty asm stops the compiler from turning it into 64 unconditional
+      // multiplies by a selected 1.
+      asm volatile("");
+      const float m_new = grow ? m_cand : m_run;
+      const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] *= alpha;
+    }
+    // Scores of the next block (the slot past the last block holds stale
+    // data; that result is never used).
+    s_nx = scores((SLOT + 1) % R);
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    float l_blk = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, neg_m));
+      l_blk += s[r];
+    }
+    l_run += l_blk;
+    const char* vb_ = reinterpret_cast<const char*>(Vs[SLOT]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pb = pack_chunk<T>(s, t);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) mfma_chunk<T>(o[b], tr_frag(vb_, vofs0[b] + t * 4096, vofs1[b] + t * 4096), pb);
+    }
+    // Blocks kb+1 .. kb+PF-1 must be in LDS for the next block; the loads of
+    // block kb+PF issued above may stay in flight.
+    if (ahead)
+      wait_vmem4();
+    else
+      wait_vmem();
+    __syncthreads();
+  };
+  // Blocks wholly below every row of this query tile and before N need no
+  // mask; the diagonal and ragged blocks come last.
+  const int nb_full = min(nb, CAUSAL ? min(q0, N) / KB : N / KB);
+  f32x16 s0 = scores(0), s1;
+  int kb = 0;
+  for (; kb + 4 <= nb_full; kb += 4) {
+    block(IntC<0>{}, kb, BoolC<false>{}, s0, s1);
+    block(IntC<1>{}, kb + 1, BoolC<false>{}, s1, s0);
+    block(IntC<2>{}, kb + 2, BoolC<false>{}, s0, s1);
+    block(IntC<3>{}, kb + 3, BoolC<false>{}, s1, s0);
+  }
+  // The rest (at most 3 full blocks, then the masked ones), slot by slot.
+  for (; kb < nb; ++kb) {
+    switch (kb & 3) {
+      case 0: block(IntC<0>{}, kb, BoolC<true>{}, s0, s1); break;
+      case 1: block(IntC<1>{}, kb, BoolC<true>{}, s0, s1); break;
+      case 2: block(IntC<2>{}, kb, BoolC<true>{}, s0, s1); break;
+      default: block(IntC<3>{}, kb, BoolC<true>{}, s0, s1); break;
+    }
+    s0 = s1;
+  }
+
+  const float l_tot = l_run + swap_halves(l_run, lane);
+  if (qi < N) {
+    const float inv = 1.0f / l_tot;
+    T* Oi = O + base + (size_t)qi * D;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * b + 8 * g + 4 * h;
+        store4<T>(Oi + d0, o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
+                  o[b][4 * g + 3] * inv);
+      }
+    }
+    if (h == 0) LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
+  if (sizeof(T) == 2 && D == 128) {
+    const int BH = a.B * a.H;
+    const int num_qt = (a.N + fpp::BR - 1) / fpp::BR;
+    const long long blocks = (long long)num_qt * BH;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, BH, num_qt,
+                       a.scale * kLog2e);
+    return hipGetLastError();
+  }
   using C = FwdTile<T, D>;
   const int BH = a.B * a.H;
   const int num_qt = (a.N + C::BR - 1) / C::BR;

@@ -71,9 +71,9 @@ int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse
 
 /*
  * Bytes of device workspace fa2_backward needs for this problem (0 for an
- * empty one).  The workspace holds D = rowsum(dO * O) as float [B,H,N] and,
- * in bf16 mode, an fp32 dQ accumulator [B,H,N,d]; its contents on entry do
- * not matter and on return are unspecified.  Returns 0 for invalid sizes.
+ * empty one).  The workspace holds D = rowsum(dO * O) and LSE * log2(e),
+ * each float [B,H,N] padded to 256 bytes; its contents on entry do not
+ * matter and on return are unspecified.  Returns 0 for invalid sizes.
  */
 size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype);
 
@@ -81,12 +81,13 @@ size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype);
  * Backward pass for the loss L = sum(O * dO).  o and lse must be the outputs
  * of fa2_forward for the same q, k, v, scale and causal.  Overwrites dq, dk,
  * dv (never accumulates into them).  Kernels, in stream order:
- *   1. D_i = sum_k dO_ik O_ik (fp32) and zeroing of the dQ accumulator;
- *   2. a key-tile-parallel kernel that recomputes P from q, k and lse,
- *      accumulates dK and dV in registers and adds dQ partial sums into the
- *      fp32 accumulator with atomics (their order varies, so dq may differ
- *      between runs in the last bits);
- *   3. in bf16 mode, conversion of the dQ accumulator to bf16.
+ *   1. D_i = sum_k dO_ik O_ik (fp32) and LSE_i * log2(e), into the workspace;
+ *   2. a key-tile-parallel kernel that recomputes P from q, k and lse and
+ *      accumulates dK and dV in registers;
+ *   3. a query-tile-parallel kernel that recomputes P and dP and accumulates
+ *      dQ in registers.
+ * No atomics: every output element is written once by one workgroup, so
+ * the results are the same bits from run to run.
  * workspace / workspace_bytes: device buffer of at least
  * fa2_backward_workspace_size(B, H, N, d, dtype) bytes, 16-byte aligned.
  */
@@ -97,10 +98,11 @@ int fa2_backward(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * One stage of fa2_backward, with exactly fa2_backward's arguments and
- * checks: stage 1 = D and accumulator zeroing, 2 = the key-tile kernel,
- * 3 = dQ conversion (a no-op in fp32 mode).  Enqueuing stages 1, 2, 3 in
- * order on one stream is fa2_backward; the split lets a caller record
- * events around the key-tile kernel.  Any other stage: FA2_ERR_INVALID_ARG.
+ * checks: stage 1 = D and LSE * log2(e), 2 = the dK/dV kernel, 3 = the dQ
+ * kernel.  Enqueuing stages 1, 2, 3 in order on one stream is fa2_backward;
+ * the split lets a caller record events around each kernel.  Stages 2 and 3
+ * read what stage 1 wrote to the workspace.  Any other stage:
+ * FA2_ERR_INVALID_ARG.
  */
 int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                        const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,

@@ -97,8 +97,8 @@ def test_workspace_size_formula(L):
         return (x + 255) // 256 * 256
     B, H, N, d = 4, 16, 4096, 128
     rows = B * H * N
-    assert L.fa2_backward_workspace_size(B, H, N, d, 1) == al(rows * 4)
-    assert L.fa2_backward_workspace_size(B, H, N, d, 0) == al(rows * 4)
+    assert L.fa2_backward_workspace_size(B, H, N, d, 1) == 2 * al(rows * 4)
+    assert L.fa2_backward_workspace_size(B, H, N, d, 0) == 2 * al(rows * 4)
     assert L.fa2_backward_workspace_size(0, H, N, d, 1) == 0
     assert L.fa2_backward_workspace_size(B, H, N, 40, 1) == 0
     assert L.fa2_backward_workspace_size(-1, H, N, d, 1) == 0

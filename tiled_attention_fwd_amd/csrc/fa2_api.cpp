@@ -79,7 +79,8 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   if (!workspace || workspace_bytes < fa2::ws_total_bytes(rows, d, dtype)) return FA2_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
   float* delta = static_cast<float*>(workspace);
-  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, delta,
+  float* lse2 = delta + fa2::align256(rows * sizeof(float)) / sizeof(float);
+  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, delta, lse2,
                  static_cast<hipStream_t>(stream)};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;

@@ -14,7 +14,7 @@
 //
 // Kernels, in stream order:
 //   bwd_pre_kernel   D = rowsum(dO o O) in fp32 (HBM-bound, one pass over O
-//                    and dO).
+//                    and dO), and LSE * log2(e) for the dK/dV kernel.
 //   bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile); each of
 //                    its 4 waves owns 32 keys and keeps K, V (as MFMA B
 //                    operands) and its dK^T, dV^T accumulators in registers
@@ -23,6 +23,9 @@
 //                    dV^T += dO^T P and dK^T += Q^T dS on MFMA, with P and dS
 //                    fed straight from the accumulator layout and Q^T, dO^T
 //                    read from the row-major LDS tiles by transpose reads.
+//                    For bf16 and d = 128, bwd_dkdv_d128_kernel runs the
+//                    same pass with direct-to-LDS loads into swizzled tiles
+//                    and two independent workgroups per CU.
 //   bwd_dq_kernel    one workgroup per (batch, head, 128-query tile), shaped
 //                    like the forward pass: S^T = K Q^T and dP^T = V dO^T on
 //                    MFMA, so each lane owns one query and its LSE and D are
@@ -67,7 +70,8 @@ __device__ __forceinline__ float dot_chunk<__bf16>(u32x4 a, u32x4 b) {
 // D_i = sum_k dO_ik O_ik.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                      float* __restrict__ Delta, long long rows) {
+                                                      const float* __restrict__ LSE, float* __restrict__ Delta,
+                                                      float* __restrict__ Lse2, long long rows) {
   constexpr int CH = Elt<T>::CH;
   constexpr int TPR = D / CH;  // threads per row (2..32, a power of two)
   constexpr int RPB = 256 / TPR;
@@ -79,7 +83,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && cc == 0) Delta[row] = acc;
+  if (row < rows && cc == 0) {
+    Delta[row] = acc;
+    Lse2[row] = LSE[row] * kLog2e;  // base-2 units, as the dK/dV kernel's exponent wants them
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -486,46 +493,46 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for bf16 with d = 128: 8 waves as two groups that alternate query
-// steps over the same 128 keys, so every SIMD runs two waves (one per group)
-// and one wave's softmax work overlaps the other's MFMAs.  Register budget
-// (<= 256 per wave): K rows and the dK^T, dV^T partial accumulators stay in
-// registers; V rows come from LDS.  Q and dO tiles (32 rows per group step,
-// double-buffered) are filled by direct global->LDS loads into unpadded
-// 256-byte rows whose 16-byte chunks are XOR-swizzled (chunk c of row r at
-// c ^ swz(r)): 16 lanes reading one chunk of 16 consecutive rows, and the
-// 4-row x 32-byte windows of a transpose read, both land on distinct banks.
-// The two groups' partial dK, dV are summed through LDS at the end.
+// dK, dV for bf16 with d = 128: one 4-wave workgroup per (batch, head,
+// 128-key tile), two workgroups per CU, so every SIMD runs two waves from
+// different workgroups whose barriers are independent: one wave's softmax
+// work can overlap the other's MFMAs without the two being held in step.
+// Register budget (<= 256 per wave): K rows and the dK^T, dV^T accumulators
+// stay in registers; V rows come from LDS.  Q and dO tiles (32 rows per
+// step, double-buffered) are filled by direct global->LDS loads into
+// unpadded 256-byte rows whose 16-byte chunks are XOR-swizzled (chunk c of
+// row r at c ^ swz(r)): the 16 lanes reading one chunk of 16 consecutive
+// rows, and the 32 lanes of a transpose read, both land on distinct banks.
 // ---------------------------------------------------------------------------
-namespace pp {
+namespace d128 {
 constexpr int D = 128;
 constexpr int ROWE = 128;  // elements per LDS row
 constexpr int BC = 128;    // keys per workgroup
-constexpr int BR = 32;     // query rows per group step
+constexpr int BR = 32;     // query rows per step
 constexpr int TILE_E = BR * ROWE;
 using namespace fa2::tiles;
-}  // namespace pp
+}  // namespace d128
 
+// Each wave owns 32 keys; all four walk every 32-row query step.
 template <bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __restrict__ Q,
-                                                              const __bf16* __restrict__ K,
-                                                              const __bf16* __restrict__ V,
-                                                              const __bf16* __restrict__ dO,
-                                                              const float* __restrict__ LSE,
-                                                              const float* __restrict__ Delta,
-                                                              __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                                                              int N, int BH, float sl2, float scale) {
-  using namespace pp;
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __restrict__ Q,
+                                                               const __bf16* __restrict__ K,
+                                                               const __bf16* __restrict__ V,
+                                                               const __bf16* __restrict__ dO,
+                                                               const float* __restrict__ Lse2,
+                                                               const float* __restrict__ Delta,
+                                                               __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                                                               int N, int BH, float sl2, float scale) {
+  using namespace d128;
   typedef __bf16 T;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
-  __shared__ __attribute__((aligned(16))) T Vs[BC * ROWE];             // 32 KB
-  __shared__ __attribute__((aligned(16))) T QdO[2][2][2][TILE_E];      // [buf][group][Q|dO], 64 KB
-  __shared__ __attribute__((aligned(16))) float LD[2][2][64];          // [buf][group][LSE 32 | D 32]
+  __shared__ __attribute__((aligned(16))) T Vs[BC * ROWE];         // 32 KB
+  __shared__ __attribute__((aligned(16))) T QdO[2][2][TILE_E];     // [buf][Q|dO], 32 KB
+  __shared__ __attribute__((aligned(16))) float LD[2][64];         // [buf][LSE2 32 | D 32]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const int grp = w >> 2, kb = w & 3;
   const int lin = blockIdx.x;
   const int kt = lin / BH;  // ascending: for causal the heaviest key tiles go first
   const int bh = lin % BH;
@@ -533,11 +540,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
   const T* Qh = Q + base;
   const T* dOh = dO + base;
   const T* Vh = V + base;
-  const float* lseh = LSE + (size_t)bh * N;
+  const float* lseh = Lse2 + (size_t)bh * N;  // LSE * log2(e)
   const float* dlh = Delta + (size_t)bh * N;
   const int kv0 = kt * BC;
-  const int kw = kv0 + 32 * kb;  // first key of this wave
-  const int kj = kw + l32;       // key owned by this lane
+  const int kw = kv0 + 32 * w;  // first key of this wave
+  const int kj = kw + l32;      // key owned by this lane
   const u32x4 rq = make_rsrc(Qh, (unsigned)N * D * 2);
   const u32x4 rdo = make_rsrc(dOh, (unsigned)N * D * 2);
 
@@ -556,58 +563,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
 
   const int n_qt = (N + BR - 1) / BR;
   const int qt_begin = CAUSAL ? kv0 / BR : 0;
-  const int n_ds = (n_qt - qt_begin + 1) / 2;  // double steps (one step per group)
+  const int n_st = n_qt - qt_begin;  // >= 1
 
-  // V tile: 32 one-kilobyte loads, 4 per wave (rows past N read row N-1).
+  // V tile: 32 one-kilobyte loads, 8 per wave (rows past N read row N-1).
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int k = 4 * w + u;
+  for (int u = 0; u < 8; ++u) {
+    const int k = 8 * w + u;
     const int r = 4 * k + (lane >> 4);
     const int c = (lane & 15) ^ swz(r);
     dload16(Vh + (size_t)min(kv0 + r, N - 1) * D + c * 8, &Vs[k * 512]);
   }
-  // Q, dO, LSE, D of double step ds into buffer buf: 2 groups x 2 tensors x
-  // 8 loads, 4 per wave; wave 0 / wave 4 fetch LSE and D of group 0 / 1.
-  // Complete 32-row steps take the row offset as the uniform buffer offset;
-  // a ragged last step clamps its rows to N-1 per lane.
-  auto issue = [&](int ds, int buf) {
+  // Q, dO, LSE2, D of step st into buffer buf: 2 tensors x 8 loads, 4 per
+  // wave (waves 0-1 Q, 2-3 dO); wave 0 fetches LSE2 and D.  Complete steps
+  // take the row offset as the uniform buffer offset; a ragged last step
+  // clamps its rows to N-1 per lane.
+  auto issue = [&](int st, int buf) {
+    const int step = qt_begin + st;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = 4 * w + u;
-      const int g = q >> 4, tens = (q >> 3) & 1, k = q & 7;
-      const int step = qt_begin + 2 * ds + g;
-      if (step < n_qt) {
-        const int r = 4 * k + (lane >> 4);
-        const int col = ((lane & 15) ^ swz(r)) * 16;
-        const u32x4 rs = tens ? rdo : rq;
-        if ((step + 1) * BR <= N)
-          bload16(rs, r * 256 + col, step * BR * 256, &QdO[buf][g][tens][k * 512]);
-        else
-          bload16(rs, min(step * BR + r, N - 1) * 256 + col, 0, &QdO[buf][g][tens][k * 512]);
-      }
+      const int tens = q >> 3, k = q & 7;
+      const int r = 4 * k + (lane >> 4);
+      const int col = ((lane & 15) ^ swz(r)) * 16;
+      const u32x4 rs = tens ? rdo : rq;
+      if ((step + 1) * BR <= N)
+        bload16(rs, r * 256 + col, step * BR * 256, &QdO[buf][tens][k * 512]);
+      else
+        bload16(rs, min(step * BR + r, N - 1) * 256 + col, 0, &QdO[buf][tens][k * 512]);
     }
-    if (kb == 0) {
-      const int step = qt_begin + 2 * ds + grp;
-      if (step < n_qt) {
-        const int i = min(step * BR + l32, N - 1);
-        dload4(h ? dlh + i : lseh + i, &LD[buf][grp][0]);
-      }
+    if (w == 0) {
+      const int i = min(step * BR + l32, N - 1);
+      dload4(h ? dlh + i : lseh + i, &LD[buf][0]);
     }
   };
 
-  if (n_ds > 0) issue(0, 0);
+  issue(0, 0);
   wait_vmem();
   __syncthreads();
 
   const SwzOffsets so = swz_offsets(lane);
-  // One group step: 32 query rows against this wave's 32 keys.
+  // One step: 32 query rows against this wave's 32 keys.
   auto step_body = [&](const T* qt, const T* gt, const float* ld, int i0, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     // Launder the lane offsets so the per-fragment XORs are recomputed each
     // step instead of being hoisted into dozens of live registers.
     int rofs = so.rofs, tofs0 = so.tofs0, tofs1 = so.tofs1, kk = so.kk;
     asm volatile("" : "+v"(rofs), "+v"(tofs0), "+v"(tofs1), "+v"(kk));
-    const char* vrow = reinterpret_cast<const char*>(Vs) + kb * 32 * 256;
+    const char* vrow = reinterpret_cast<const char*>(Vs) + w * 32 * 256;
     f32x16 s = f32x16{}, dp = f32x16{};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -616,7 +618,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
       mfma_chunk<T>(s, lds16(qt, ro), kf[c]);
       mfma_chunk<T>(dp, lds16(gt, ro), lds16(vrow, ro));
     }
-    // reads of chunk c+1 (3) issued before the two products of chunk c
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
     for (int c = 0; c < DCH - 2; ++c) {
@@ -625,8 +626,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // Row of accumulator r is i0 + 4h + (8*(r/4) + r%4); the mask compares
-    // two per-lane thresholds against that compile-time constant.
     const int t_causal = kj - i0 - 4 * h;  // masked when t_causal > c_r
     const int t_rows = N - i0 - 4 * h;     // masked when c_r >= t_rows
     const bool key_dead = kj >= N;
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 4 * g + q;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q] * kLog2e));
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
         if (MASKED) {
           const int c_r = 8 * g + q;
           p = ((CAUSAL & (t_causal > c_r)) | (c_r >= t_rows) | key_dead) ? 0.f : p;
@@ -659,7 +658,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
         mfma_chunk<T>(dk[b], tr_frag(qt, tofs0 + cb, tofs1 + cb), sb);
       }
     }
-    // fragments two products ahead: 4 reads, then (product, 2 reads) x 14, 2 products
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
     for (int i = 0; i < 13; ++i) {
@@ -670,59 +668,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto double_step = [&](int ds, auto masked) {
-    const int buf = ds & 1;
-    if (ds + 1 < n_ds) issue(ds + 1, buf ^ 1);
-    const int step = qt_begin + 2 * ds + grp;
-    if (step < n_qt) {
-      const int i0 = step * BR;
-      // Skip blocks with no visible key (all above the diagonal, or keys
-      // past N); they would only add zeros.
-      if (!decltype(masked)::value || (kw < N && (!CAUSAL || i0 + 31 >= kw)))
-        step_body(QdO[buf][grp][0], QdO[buf][grp][1], LD[buf][grp], i0, masked);
-    }
+  auto step = [&](int st, auto masked) {
+    const int buf = st & 1;
+    if (st + 1 < n_st) issue(st + 1, buf ^ 1);
+    const int i0 = (qt_begin + st) * BR;
+    // Skip blocks with no visible key (all above the diagonal, or keys past
+    // N); they would only add zeros.
+    if (!decltype(masked)::value || (kw < N && (!CAUSAL || i0 + 31 >= kw)))
+      step_body(QdO[buf][0], QdO[buf][1], LD[buf], i0, masked);
     wait_vmem();
     __syncthreads();
   };
-  // Double steps whose two query steps are both off the diagonal band, both
-  // complete (32 rows < N) and on a complete key tile need no mask; only a
-  // prefix (the diagonal) and a suffix (the ragged end) do.
+  // Steps off the diagonal band, complete (32 rows < N) and on a complete key
+  // tile need no mask; only a prefix (the diagonal) and the ragged end do.
   const int full_steps = N / BR - qt_begin;
-  const int ds_bulk_begin = (kv0 + BC > N) ? n_ds : (CAUSAL ? min(n_ds, 2) : 0);
-  const int ds_bulk_end = max(ds_bulk_begin, min(n_ds, full_steps / 2));
-  int ds = 0;
-  for (; ds < ds_bulk_begin; ++ds) double_step(ds, BoolC<true>{});
-  for (; ds < ds_bulk_end; ++ds) double_step(ds, BoolC<false>{});
-  for (; ds < n_ds; ++ds) double_step(ds, BoolC<true>{});
-
-  // Sum the two groups' partial accumulators through LDS (reusing QdO).
-  float* red = reinterpret_cast<float*>(&QdO[0][0][0][0]);  // 16384 floats
-  auto reduce = [&](f32x16 (&acc)[NB]) {
-    if (grp == 1) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[((kb * NB + b) * 16 + r) * 64 + lane] = acc[b][r];
-    }
-    __syncthreads();
-    if (grp == 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] += red[((kb * NB + b) * 16 + r) * 64 + lane];
-    }
-    __syncthreads();
-  };
-  reduce(dk);
-  reduce(dv);
+  const int st_bulk_begin = (kv0 + BC > N) ? n_st : (CAUSAL ? min(n_st, BC / BR) : 0);
+  const int st_bulk_end = max(st_bulk_begin, min(n_st, full_steps));
+  int st = 0;
+  for (; st < st_bulk_begin; ++st) step(st, BoolC<true>{});
+  for (; st < st_bulk_end; ++st) step(st, BoolC<false>{});
+  for (; st < n_st; ++st) step(st, BoolC<true>{});
 
   // Stage the bf16 results row-major in LDS (16-byte chunks swizzled like
-  // the tiles): dK in the V tile, dV in the first 32 KB of the Q/dO buffers,
-  // both free now.  Then all eight waves store whole 256-byte rows.
+  // the tiles): dK in the V tile, dV in the Q/dO buffers, both free now.
   T* sk = Vs;
-  T* sv = &QdO[0][0][0][0];
-  if (grp == 0) {
-    const int row = 32 * kb + l32;
+  T* sv = &QdO[0][0][0];
+  {
+    const int row = 32 * w + l32;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -736,8 +708,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(const __bf16* __res
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * w + 4 * i + (lane >> 4);
+  for (int i = 0; i < 8; ++i) {
+    const int row = 32 * w + 4 * i + (lane >> 4);
     const int ch = lane & 15;
     const int key = kv0 + row;
     if (key < N) {
@@ -756,15 +728,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   if (stage == 1) {
     constexpr int RPB = 256 / (D / Elt<T>::CH);
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.delta, rows);
+                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.lse, a.delta, a.lse2,
+                       rows);
     return hipGetLastError();
   }
   if (stage == 2 && sizeof(T) == 2 && D == 128) {
-    const long long blocks = (long long)((a.N + pp::BC - 1) / pp::BC) * BH;
+    const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BH;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_pp_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_d128_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse, a.delta,
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
                        static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, sl2, a.scale);
     return hipGetLastError();
   }

@@ -39,13 +39,15 @@ struct BwdArgs {
   float scale;
   bool causal;
   int dtype;
-  float* delta;  // [B, H, N] inside the workspace
+  float* delta;  // D = rowsum(dO * O), [B, H, N] inside the workspace
+  float* lse2;   // LSE * log2(e), [B, H, N] inside the workspace
   hipStream_t stream;
 };
 
-// Workspace layout: D = rowsum(dO * O) as float [B, H, N], padded to 256 B.
+// Workspace layout: D = rowsum(dO * O), then LSE * log2(e), each float
+// [B, H, N] padded to 256 B.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return align256(rows * sizeof(float)); }
+inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return 2 * align256(rows * sizeof(float)); }
 
 hipError_t launch_forward(const FwdArgs& a);
 // stage 1: D = rowsum(dO * O); 2: the dK/dV kernel; 3: the dQ kernel.

@@ -29,7 +29,9 @@
 //   bwd_dq_kernel    one workgroup per (batch, head, 128-query tile), shaped
 //                    like the forward pass: S^T = K Q^T and dP^T = V dO^T on
 //                    MFMA, so each lane owns one query and its LSE and D are
-//                    scalars, then dQ^T += K^T dS^T.
+//                    scalars, then dQ^T += K^T dS^T.  For bf16 and d = 128,
+//                    bwd_dq_d128_kernel runs it over a ring of direct-loaded
+//                    32-key blocks, like the bf16 d = 128 forward.
 // The two halves recompute S and dP instead of exchanging dS, so dQ needs no
 // atomics or fp32 accumulator and the result is deterministic.
 // Causal: tiles start and stop at the diagonal, blocks entirely above it
@@ -720,6 +722,182 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
   }
 }
 
+// dQ for bf16 and d = 128: the pass of bwd_dq_kernel organised like the bf16
+// d = 128 forward.  32-key blocks of K and V reach LDS through direct loads
+// into a ring of 4 slots (unpadded swizzled rows), issued 3 blocks ahead,
+// one barrier per block; lane offsets of every fragment and load are
+// computed once and the block loop is unrolled over the ring.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const __bf16* __restrict__ Q,
+                                                              const __bf16* __restrict__ K,
+                                                              const __bf16* __restrict__ V,
+                                                              const __bf16* __restrict__ dO,
+                                                              const float* __restrict__ Lse2,
+                                                              const float* __restrict__ Delta,
+                                                              __bf16* __restrict__ dQ, int N, int BH, int num_qt,
+                                                              float sl2, float scale) {
+  using namespace tiles;
+  typedef __bf16 T;
+  constexpr int D = 128, KB = 32, BLK_E = KB * 128, CH = 8, DCH = D / 16, NB = D / 32;
+  constexpr int QB = 128;           // query rows per workgroup (4 waves x 32)
+  constexpr int R = 4, PF = R - 1;  // ring slots, blocks loaded ahead
+  __shared__ __attribute__((aligned(16))) T Ks[R][BLK_E];
+  __shared__ __attribute__((aligned(16))) T Vs[R][BLK_E];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int lin = blockIdx.x;
+  const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
+  const int bh = lin % BH;
+  const size_t base = (size_t)bh * N * D;
+  const int q0 = qt * QB;
+  const int qw = q0 + 32 * w;  // first query row of this wave
+  const int qi = qw + l32;     // query row (column of S^T) owned by this lane
+  // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
+  // q = 4w + u, rows 4(q%8)..+3 of the block.
+  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + base, (unsigned)N * D * 2);
+  T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
+
+  const int kv_end = CAUSAL ? min(N, q0 + QB) : N;
+  const int nb = (kv_end + KB - 1) / KB;
+
+  // Per-lane constants: load offsets within a block and LDS fragment offsets
+  // (row fragments by chunk, transpose fragments by column block and half).
+  int voff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
+    voff[u] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+  }
+  const SwzOffsets so = swz_offsets(lane);
+  int kofs[DCH], tofs0[NB], tofs1[NB];
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) kofs[c] = so.rofs ^ (c << 5);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    tofs0[b] = so.tofs0 + ((b ^ so.kk) << 6);
+    tofs1[b] = so.tofs1 + ((b ^ so.kk) << 6);
+  }
+  // Block kb into slot (rows past N read row N-1; their keys are masked).
+  auto issue = [&](int kb, int slot) {
+    const int row0 = kb * KB;
+    T* dst = dst0 + slot * BLK_E;
+    if (row0 + KB <= N) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bload16(rsrc, voff[u], row0 * 256, dst + ((4 * w + u) & 7) * 512);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
+        bload16(rsrc, min(row0 + r, N - 1) * 256 + (voff[u] & 255), 0, dst + ((4 * w + u) & 7) * 512);
+      }
+    }
+  };
+
+  // Q and dO rows of this lane (B operands), its LSE (base 2) and D.  Rows
+  // past N read row N-1 and are never stored.
+  const int qc = min(qi, N - 1);
+  u32x4 qf[DCH], gf[DCH];
+  {
+    const size_t off = base + (size_t)qc * D + h * CH;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      qf[c] = load16(Q + off + c * 2 * CH);
+      gf[c] = load16(dO + off + c * 2 * CH);
+    }
+  }
+  const float lse2 = Lse2[(size_t)bh * N + qc];
+  const float dl = Delta[(size_t)bh * N + qc];
+#pragma unroll
+  for (int b = 0; b < PF; ++b)
+    if (b < nb) issue(b, b);
+  wait_vmem();
+  __syncthreads();
+
+  // S^T = K Q^T and dP^T = V dO^T for the block in slot.
+  auto products = [&](int slot, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+    const char* kb_ = reinterpret_cast<const char*>(Ks[slot]);
+    const char* vb_ = reinterpret_cast<const char*>(Vs[slot]);
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      mfma_chunk<T>(s, lds16(kb_, kofs[c]), qf[c]);
+      mfma_chunk<T>(dp, lds16(vb_, kofs[c]), gf[c]);
+    }
+  };
+
+  f32x16 dq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
+
+  // Block kb in slot SLOT: its products, dS^T = P^T (dP^T - D) and
+  // dQ^T += K^T dS^T.  (The Q and dO rows and the dQ accumulators leave no
+  // room for a second block's products in flight.)
+  auto block = [&](auto slotc, int kb, auto masked) {
+    constexpr int SLOT = decltype(slotc)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    const bool ahead = kb + PF < nb;
+    if (ahead) issue(kb + PF, (SLOT + PF) % R);
+    f32x16 s, dp;
+    products(SLOT, s, dp);
+    const int k0 = kb * KB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+      if (MASKED) {
+        const int j = k0 + acc_row(r, h);
+        p = ((CAUSAL & (j > qi)) | (j >= N)) ? 0.f : p;  // a select, not a branch
+      }
+      dp[r] = p * (dp[r] - dl);
+    }
+    const char* kb_ = reinterpret_cast<const char*>(Ks[SLOT]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 sb = pack_chunk<T>(dp, t);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) mfma_chunk<T>(dq[b], tr_frag(kb_, tofs0[b] + t * 4096, tofs1[b] + t * 4096), sb);
+    }
+    if (ahead)
+      wait_vmem4();
+    else
+      wait_vmem();
+    __syncthreads();
+  };
+  // Blocks wholly below every row of this query tile and before N need no
+  // mask; the diagonal and ragged blocks come last.
+  const int nb_full = min(nb, CAUSAL ? min(q0, N) / KB : N / KB);
+  int kb = 0;
+  for (; kb + 4 <= nb_full; kb += 4) {
+    block(IntC<0>{}, kb, BoolC<false>{});
+    block(IntC<1>{}, kb + 1, BoolC<false>{});
+    block(IntC<2>{}, kb + 2, BoolC<false>{});
+    block(IntC<3>{}, kb + 3, BoolC<false>{});
+  }
+  for (; kb < nb; ++kb) {
+    switch (kb & 3) {
+      case 0: block(IntC<0>{}, kb, BoolC<true>{}); break;
+      case 1: block(IntC<1>{}, kb, BoolC<true>{}); break;
+      case 2: block(IntC<2>{}, kb, BoolC<true>{}); break;
+      default: block(IntC<3>{}, kb, BoolC<true>{}); break;
+    }
+  }
+
+  if (qi < N) {
+    T* dQi = dQ + base + (size_t)qi * D;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * b + 8 * g + 4 * h;
+        store4<T>(dQi + d0, dq[b][4 * g] * scale, dq[b][4 * g + 1] * scale, dq[b][4 * g + 2] * scale,
+                  dq[b][4 * g + 3] * scale);
+      }
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
@@ -749,6 +927,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
                        a.N, BH, sl2, a.scale);
+    return hipGetLastError();
+  }
+  if (stage == 3 && sizeof(T) == 2 && D == 128) {
+    const int num_qt = (a.N + 127) / 128;
+    const long long blocks = (long long)num_qt * BH;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_d128_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
+                       static_cast<__bf16*>(a.dq), a.N, BH, num_qt, sl2, a.scale);
     return hipGetLastError();
   }
   if (stage == 3) {

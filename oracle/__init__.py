@@ -61,9 +61,12 @@ class Oracle:
         return int(self.lib.oracle_max_threads())
 
     def fwd(self, q, k, v, scale: float, causal: bool):
-        """Return (O, LSE) in fp64 for [B, H, N, d] inputs (numpy or CPU torch)."""
+        """Return (O, LSE) in fp64 for q [B, H, N, d] and k, v [B, H_kv, N, d]
+        (numpy or CPU torch); H_kv divides H (H_kv < H: grouped-query
+        attention, see _expand_kv)."""
         q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
         B, H, N, d = _shape(q)
+        k, v = _expand_kv(k, H), _expand_kv(v, H)
         if k.shape != q.shape or v.shape != q.shape:
             raise ValueError("q, k, v shapes differ")
         o = np.empty_like(q)
@@ -75,9 +78,12 @@ class Oracle:
         return o, lse
 
     def bwd(self, q, k, v, dO, scale: float, causal: bool, return_delta: bool = False):
-        """Return (dQ, dK, dV[, D]) in fp64 for the loss L = sum(O * dO)."""
+        """Return (dQ, dK, dV[, D]) in fp64 for the loss L = sum(O * dO); with
+        k, v of H_kv < H heads, dK and dV are [B, H_kv, N, d]."""
         q, k, v, dO = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dO)
         B, H, N, d = _shape(q)
+        H_kv = k.shape[1] if k.ndim == 4 else H
+        k, v = _expand_kv(k, H), _expand_kv(v, H)
         for t in (k, v, dO):
             if t.shape != q.shape:
                 raise ValueError("input shapes differ")
@@ -88,6 +94,7 @@ class Oracle:
                                      int(bool(causal)))
         if rc != 0:
             raise RuntimeError("oracle_bwd_f64 failed with code %d" % rc)
+        dk, dv = _reduce_kv(dk, H_kv), _reduce_kv(dv, H_kv)
         if return_delta:
             return dq, dk, dv, delta
         return dq, dk, dv
@@ -111,6 +118,31 @@ def fwd(q, k, v, scale: float, causal: bool):
 def bwd(q, k, v, dO, scale: float, causal: bool, return_delta: bool = False):
     """(dQ, dK, dV[, D]) from the default oracle library."""
     return default().bwd(q, k, v, dO, scale, causal, return_delta)
+
+
+def _expand_kv(t: np.ndarray, H: int) -> np.ndarray:
+    """Grouped-query attention (named, not defined, in the article's section
+    "Next Frontiers in WebGPU ML", "Broader Opset Support"), read as: query
+    head h uses key/value head h // (H / H_kv), i.e. consecutive groups of
+    H / H_kv query heads share one K, V head.  It is exactly multi-head
+    attention on K and V with each head repeated H / H_kv times."""
+    if t.ndim != 4:
+        raise ValueError("expected [B, H, N, d] arrays, got shape %r" % (t.shape,))
+    H_kv = t.shape[1]
+    if H_kv == H:
+        return t
+    if H_kv <= 0 or H % H_kv != 0:
+        raise ValueError("key/value heads (%d) must divide query heads (%d)" % (H_kv, H))
+    return np.ascontiguousarray(np.repeat(t, H // H_kv, axis=1))
+
+
+def _reduce_kv(g: np.ndarray, H_kv: int) -> np.ndarray:
+    """Gradient of a K or V head shared by a group: the sum over the group's
+    repeated copies (chain rule through the repeat in _expand_kv)."""
+    B, H, N, d = g.shape
+    if H_kv == H:
+        return g
+    return np.ascontiguousarray(g.reshape(B, H_kv, H // H_kv, N, d).sum(axis=2))
 
 
 def _as_f64(x) -> np.ndarray:

@@ -51,10 +51,12 @@ def torch_reference(q, k, v, dO, scale, causal):
     qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
     kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
     vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
-    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale)
+    gqa = kt.shape[1] != qt.shape[1]
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale, enable_gqa=gqa)
     (o * torch.tensor(dO, dtype=torch.float64)).sum().backward()
     with torch.no_grad():
-        logits = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
+        kx = kt.repeat_interleave(qt.shape[1] // kt.shape[1], dim=1) if gqa else kt
+        logits = scale * torch.matmul(qt, kx.transpose(-1, -2).contiguous())
         if causal:
             n = q.shape[-2]
             mask = torch.ones(n, n, dtype=torch.bool).triu(1)
@@ -252,6 +254,39 @@ def pin_finite_diff(orc, shape=(1, 1, 6, 3), causal=True, seed=19, sample=None, 
     return worst
 
 
+# --------------------------------------------------------------------------
+# grouped-query attention (the article's "Next Frontiers in WebGPU ML",
+# "Broader Opset Support", names it; query head h reads K, V head h // G)
+# --------------------------------------------------------------------------
+def pin_gqa_torch(orc):
+    """GQA (H=4 over 2 K/V heads, causal) and MQA (H=3 over 1, unmasked)
+    against torch float64 SDPA with enable_gqa and autograd."""
+    q, g = randn((2, 4, 19, 8), 40), randn((2, 4, 19, 8), 41)
+    k, v = randn((2, 2, 19, 8), 42), randn((2, 2, 19, 8), 43)
+    pin_torch(orc, q, k, v, g, 0.35, True)
+    q, g = randn((1, 3, 12, 4), 44), randn((1, 3, 12, 4), 45)
+    k, v = randn((1, 1, 12, 4), 46), randn((1, 1, 12, 4), 47)
+    pin_torch(orc, q, k, v, g, 0.5, False)
+
+
+def pin_gqa_shared_heads(orc, seed=48, H=3, N=9, d=4):
+    """MQA with every query head equal and every dO head equal: each output
+    head is the single-head result, and the shared K, V receive the sum of
+    the heads' gradients, i.e. H times the single-head dK, dV."""
+    q1, g1 = randn((1, 1, N, d), seed), randn((1, 1, N, d), seed + 1)
+    k, v = randn((1, 1, N, d), seed + 2), randn((1, 1, N, d), seed + 3)
+    q, g = np.repeat(q1, H, axis=1), np.repeat(g1, H, axis=1)
+    o1, l1 = orc.fwd(q1, k, v, 0.4, True)
+    dq1, dk1, dv1 = orc.bwd(q1, k, v, g1, 0.4, True)
+    o, lse = orc.fwd(q, k, v, 0.4, True)
+    dq, dk, dv = orc.bwd(q, k, v, g, 0.4, True)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    for h in range(H):
+        assert rel_err(o[:, h:h + 1], o1) < 1e-14 and rel_err(lse[:, h:h + 1], l1) < 1e-14
+        assert rel_err(dq[:, h:h + 1], dq1) < 1e-14
+    assert rel_err(dk, H * dk1) < 1e-13 and rel_err(dv, H * dv1) < 1e-13
+
+
 ALL_SMALL_PINS = [
     pin_uniform_v, pin_direct_lse, pin_causal_row0, pin_q_zero, pin_single_key, pin_two_keys,
     pin_invariants, pin_permutation,
@@ -259,4 +294,5 @@ ALL_SMALL_PINS = [
     lambda orc: pin_finite_diff(orc, (1, 1, 5, 2), False),
     lambda orc: pin_torch(orc, *(randn((1, 2, 33, 8), 20 + t) for t in range(4)), 0.35, True),
     lambda orc: pin_torch(orc, *(randn((1, 2, 33, 8), 30 + t) for t in range(4)), 0.35, False),
+    pin_gqa_torch, pin_gqa_shared_heads,
 ]

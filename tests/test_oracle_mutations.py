@@ -10,6 +10,7 @@ oracle unchecked.
 """
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -62,3 +63,26 @@ def test_pins_catch_mutation(tmp_path, name):
 
 def test_unmutated_oracle_passes_every_pin():
     assert _caught(oracle.default()) == []
+
+
+# Mistakes in the grouped-query layer of the oracle (Python): the shared
+# K, V gradient averaged instead of summed, and query heads mapped to K, V
+# heads round-robin (h % H_kv) instead of in consecutive groups (h // G).
+def _mean_reduce(g, H_kv):
+    B, H, N, d = g.shape
+    if H_kv == H:
+        return g
+    return g.reshape(B, H_kv, H // H_kv, N, d).mean(axis=2)
+
+
+def _roundrobin_expand(t, H):
+    if t.shape[1] == H:
+        return t
+    return np.ascontiguousarray(np.tile(t, (1, H // t.shape[1], 1, 1)))
+
+
+@pytest.mark.parametrize("name,attr,fn", [("gqa_grad_mean", "_reduce_kv", _mean_reduce),
+                                          ("gqa_roundrobin_heads", "_expand_kv", _roundrobin_expand)])
+def test_pins_catch_gqa_mutation(monkeypatch, name, attr, fn):
+    monkeypatch.setattr(oracle, attr, fn)
+    assert _caught(oracle.default()), "no pin detects the planted mistake %r" % name

@@ -109,6 +109,42 @@ int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, c
                        int H, int N, int d, float scale, int causal, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * Grouped-query and multi-query attention.  The article "Revolutionizing
+ * Web-Based AI: How a Plain JavaScript Prototype Paved the Way for
+ * High-Performance WebGPU Flash Attention 2" names grouped-query attention
+ * as the next primitive to build (section "Next Frontiers in WebGPU ML",
+ * "Broader Opset Support") without defining it; the reading taken: the
+ * H query heads form H_kv consecutive groups of G = H / H_kv, and query
+ * head h uses key/value head h / G (H_kv = 1: multi-query attention;
+ * H_kv = H: exactly fa2_forward / fa2_backward).
+ *
+ * Same arguments, layouts and behaviour as the calls above except:
+ *   H_kv   number of key/value heads; 1 <= H_kv and H_kv divides H (both 0
+ *          when H is 0), else FA2_ERR_INVALID_ARG.
+ *   k, v   [B, H_kv, N, d]; dk, dv (backward) [B, H_kv, N, d], each the sum
+ *          of the gradients of the group's query heads, written once
+ *          (overwritten, never accumulated into).
+ *   q, o, dO, dq [B, H, N, d] and lse [B, H, N] as before; the workspace
+ *          size is fa2_backward_workspace_size(B, H, N, d, dtype).
+ * The dK/dV kernel walks the query heads of a group in one workgroup per
+ * key tile, so no atomics are used and results are the same bits from run
+ * to run.
+ */
+int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+                   void* stream);
+
+int fa2_backward_ex(const void* q, const void* k, const void* v, const void* o,
+                    const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                    int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o,
+                          const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                          int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

@@ -32,8 +32,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert names == ["fa2_backward", "fa2_backward_stage", "fa2_backward_workspace_size", "fa2_forward",
-                     "fa2_status_string"]
+    assert names == ["fa2_backward", "fa2_backward_ex", "fa2_backward_stage", "fa2_backward_stage_ex",
+                     "fa2_backward_workspace_size", "fa2_forward", "fa2_forward_ex", "fa2_status_string"]
     for n in names:
         assert hasattr(L, n), n
 
@@ -131,3 +131,35 @@ def test_backward_stage_validates_like_backward(L):
         == fa.FA2_ERR_UNSUPPORTED
     assert L.fa2_backward_stage(1, A, A, A, A, A, A, A, A, A, 1, 2, 64, 64, 0.125, 1, 1, A, n - 1, None) \
         == fa.FA2_ERR_WORKSPACE
+
+
+# Grouped-query entry points: H_kv must divide H (validated before any HIP
+# call, so these run without a GPU).
+def fwd_ex(L, H=4, H_kv=2, ptr=A, **over):
+    p = dict(B=1, N=64, d=64, scale=0.125, causal=1, dtype=1)
+    p.update(over)
+    return L.fa2_forward_ex(ptr, ptr, ptr, ptr, ptr, p["B"], H, H_kv, p["N"], p["d"], p["scale"], p["causal"],
+                            p["dtype"], None)
+
+
+def bwd_ex(L, H=4, H_kv=2, ptr=A, stage=None):
+    wsb = L.fa2_backward_workspace_size(1, H, 64, 64, 1)
+    args = (ptr,) * 9 + (1, H, H_kv, 64, 64, 0.125, 1, 1, A, wsb, None)
+    if stage is None:
+        return L.fa2_backward_ex(*args)
+    return L.fa2_backward_stage_ex(stage, *args)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 3), (4, 0), (4, -1), (4, 8), (6, 4)])
+def test_ex_rejects_bad_kv_heads(L, H, H_kv):
+    assert fwd_ex(L, H, H_kv) == fa.FA2_ERR_INVALID_ARG
+    assert bwd_ex(L, H, H_kv) == fa.FA2_ERR_INVALID_ARG
+    assert bwd_ex(L, H, H_kv, stage=2) == fa.FA2_ERR_INVALID_ARG
+
+
+def test_ex_checks_like_the_plain_calls(L):
+    assert fwd_ex(L, 4, 2, ptr=None) == fa.FA2_ERR_INVALID_ARG
+    assert fwd_ex(L, 4, 2, ptr=MIS) == fa.FA2_ERR_UNSUPPORTED
+    assert fwd_ex(L, 4, 2, d=48) == fa.FA2_ERR_UNSUPPORTED
+    assert fwd_ex(L, 0, 0, B=1) == fa.FA2_OK  # empty: a no-op
+    assert bwd_ex(L, 4, 1, stage=4) == fa.FA2_ERR_INVALID_ARG

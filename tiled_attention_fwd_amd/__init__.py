@@ -6,8 +6,11 @@ used for device memory and the current stream.  There is no fallback: if the
 library is not built, importing works but every call raises ``Fa2Error``.
 
 Functions with the C names (``fa2_forward``, ``fa2_backward``,
-``fa2_backward_workspace_size``, ``fa2_status_string``) take caller-allocated
-tensors like the C ABI; ``forward`` / ``backward`` allocate the outputs.
+``fa2_backward_stage``, their ``_ex`` forms with a key/value head count for
+grouped-query attention, ``fa2_backward_workspace_size``,
+``fa2_status_string``) take caller-allocated tensors like the C ABI;
+``forward`` / ``backward`` allocate the outputs (K and V may have fewer heads
+than Q: H_kv dividing H).
 """
 from __future__ import annotations
 
@@ -51,6 +54,13 @@ def lib() -> ctypes.CDLL:
         L.fa2_backward.restype = i
         L.fa2_backward_stage.argtypes = [i] + L.fa2_backward.argtypes
         L.fa2_backward_stage.restype = i
+        L.fa2_forward_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa2_forward_ex.restype = i
+        L.fa2_backward_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp,
+                                      ctypes.c_size_t, vp]
+        L.fa2_backward_ex.restype = i
+        L.fa2_backward_stage_ex.argtypes = [i] + L.fa2_backward_ex.argtypes
+        L.fa2_backward_stage_ex.restype = i
         L.fa2_backward_workspace_size.argtypes = [i, i, i, i, i]
         L.fa2_backward_workspace_size.restype = ctypes.c_size_t
         L.fa2_status_string.argtypes = [i]
@@ -96,20 +106,48 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _heads(q, k, v, *qlike):
+    """(B, H, H_kv, N, d) after checking q-shaped and k-shaped arguments."""
+    B, H, N, d = q.shape
+    if k.dim() != 4:
+        raise ValueError("expected [B, H_kv, N, d] keys, got %s" % (tuple(k.shape),))
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d) or v.shape != k.shape or H_kv == 0 and H != 0 or H_kv and H % H_kv:
+        raise ValueError("k, v must be [B, H_kv, N, d] with H_kv dividing H = %d" % H)
+    for t in (k, v) + tuple(qlike):
+        if t.dtype != q.dtype:
+            raise ValueError("all tensors must share one dtype")
+    for t in qlike:
+        if t.shape != q.shape:
+            raise ValueError("o, dO, dq must have q's shape")
+    return B, H, H_kv, N, d
+
+
 def fa2_forward(q, k, v, o, lse, causal: bool = True, scale: float | None = None, stream=None) -> None:
     """Enqueue the forward pass into caller-allocated ``o`` and ``lse``."""
+    _forward_call(False, q, k, v, o, lse, causal, scale, stream)
+
+
+def fa2_forward_ex(q, k, v, o, lse, causal: bool = True, scale: float | None = None, stream=None) -> None:
+    """As ``fa2_forward`` with k, v of H_kv heads ([B, H_kv, N, d])."""
+    _forward_call(True, q, k, v, o, lse, causal, scale, stream)
+
+
+def _forward_call(ex, q, k, v, o, lse, causal, scale, stream):
     _check_tensors(q, k, v, o, lse)
-    B, H, N, d = q.shape
-    for t in (k, v, o):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o must share shape and dtype")
+    B, H, H_kv, N, d = _heads(q, k, v, o)
+    if not ex and H_kv != H:
+        raise ValueError("fa2_forward needs H_kv == H; use fa2_forward_ex")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, H, N]")
-    st = lib().fa2_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                           B, H, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype),
-                           _stream(stream, q.device))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    tail = (N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype), _stream(stream, q.device))
+    if ex:
+        st = lib().fa2_forward_ex(*ptrs, B, H, H_kv, *tail)
+    else:
+        st = lib().fa2_forward(*ptrs, B, H, *tail)
     if st != FA2_OK:
-        raise Fa2Error(st, "fa2_forward")
+        raise Fa2Error(st, "fa2_forward_ex" if ex else "fa2_forward")
 
 
 def fa2_backward_workspace_size(B: int, H: int, N: int, d: int, dtype) -> int:
@@ -120,53 +158,74 @@ def fa2_backward_workspace_size(B: int, H: int, N: int, d: int, dtype) -> int:
 def fa2_backward(q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True, scale: float | None = None,
                  workspace: torch.Tensor | None = None, stream=None) -> None:
     """Enqueue the backward pass into caller-allocated ``dq``, ``dk``, ``dv``."""
-    _backward_call(0, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+    _backward_call(False, 0, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True, scale: float | None = None,
+                    workspace: torch.Tensor | None = None, stream=None) -> None:
+    """As ``fa2_backward`` with k, v, dk, dv of H_kv heads."""
+    _backward_call(True, 0, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
 
 
 def fa2_backward_stage(stage: int, q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True,
                        scale: float | None = None, workspace: torch.Tensor | None = None,
                        stream=None) -> None:
-    """Enqueue one backward stage (1: D, 2: key-tile kernel, 3: dQ convert)."""
+    """Enqueue one backward stage (1: D and LSE*log2(e), 2: dK/dV, 3: dQ)."""
     if workspace is None:
         raise ValueError("the stages share state through the workspace: pass one")
-    _backward_call(int(stage), q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+    _backward_call(False, int(stage), q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
 
 
-def _backward_call(stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream):
+def fa2_backward_stage_ex(stage: int, q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True,
+                          scale: float | None = None, workspace: torch.Tensor | None = None,
+                          stream=None) -> None:
+    """As ``fa2_backward_stage`` with k, v, dk, dv of H_kv heads."""
+    if workspace is None:
+        raise ValueError("the stages share state through the workspace: pass one")
+    _backward_call(True, int(stage), q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def _backward_call(ex, stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream):
     _check_tensors(q, k, v, o, dO, lse, dq, dk, dv)
-    B, H, N, d = q.shape
-    for t in (k, v, o, dO, dq, dk, dv):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o, dO, dq, dk, dv must share shape and dtype")
+    B, H, H_kv, N, d = _heads(q, k, v, o, dO, dq)
+    if dk.shape != k.shape or dv.shape != k.shape or dk.dtype != q.dtype or dv.dtype != q.dtype:
+        raise ValueError("dk, dv must have k's shape and q's dtype")
+    if not ex and H_kv != H:
+        raise ValueError("fa2_backward needs H_kv == H; use fa2_backward_ex")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, H, N]")
     need = fa2_backward_workspace_size(B, H, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
-            _dtype_code(q.dtype), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            _stream(stream, q.device))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    tail = (N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    heads = (B, H, H_kv) if ex else (B, H)
+    L = lib()
     if stage == 0:
-        st = lib().fa2_backward(*args)
+        st = (L.fa2_backward_ex if ex else L.fa2_backward)(*ptrs, *heads, *tail)
     else:
-        st = lib().fa2_backward_stage(stage, *args)
+        st = (L.fa2_backward_stage_ex if ex else L.fa2_backward_stage)(stage, *ptrs, *heads, *tail)
     if st != FA2_OK:
-        raise Fa2Error(st, "fa2_backward" if stage == 0 else "fa2_backward_stage(%d)" % stage)
+        name = ("fa2_backward" if stage == 0 else "fa2_backward_stage(%d)" % stage) + ("_ex" if ex else "")
+        raise Fa2Error(st, name)
 
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
-    """Return (o, lse) for [B, H, N, d] float32 or bfloat16 GPU tensors."""
+    """Return (o, lse) for q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv
+    dividing H) float32 or bfloat16 GPU tensors."""
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa2_forward(q, k, v, o, lse, causal, scale, stream)
+    fa2_forward_ex(q, k, v, o, lse, causal, scale, stream)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dO, causal: bool = True, scale: float | None = None,
              workspace: torch.Tensor | None = None, stream=None):
-    """Return (dq, dk, dv) of L = sum(o * dO); o, lse come from ``forward``."""
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    fa2_backward(q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+    """Return (dq, dk, dv) of L = sum(o * dO); o, lse come from ``forward``;
+    dk, dv have k's shape."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
     return dq, dk, dv

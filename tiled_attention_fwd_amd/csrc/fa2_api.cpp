@@ -29,6 +29,9 @@ int check_sizes(int B, int H, int N, int d, int dtype) {
 
 bool is_empty(int B, int H, int N) { return B == 0 || H == 0 || N == 0; }
 
+// Key/value heads: 1 <= H_kv, and H_kv divides H (both may be 0 when H is).
+bool valid_hkv(int H, int H_kv) { return H == 0 ? H_kv >= 0 : (H_kv >= 1 && H % H_kv == 0); }
+
 }  // namespace
 
 extern "C" {
@@ -44,17 +47,23 @@ const char* fa2_status_string(int status) {
   }
 }
 
-int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                float scale, int causal, int dtype, void* stream) {
+int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                   int N, int d, float scale, int causal, int dtype, void* stream) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
+  if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
   if (is_empty(B, H, N)) return FA2_OK;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA2_ERR_UNSUPPORTED;
-  fa2::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, static_cast<hipStream_t>(stream)};
+  fa2::FwdArgs a{q, k, v, o, lse, B, H, N, d, H_kv, scale, causal != 0, dtype, static_cast<hipStream_t>(stream)};
   return fa2::launch_forward(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, int dtype, void* stream) {
+  return fa2_forward_ex(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
 }
 
 size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
@@ -65,10 +74,11 @@ size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
 
 static int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v,
                          const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
-                         int H, int N, int d, float scale, int causal, int dtype, void* workspace,
+                         int H, int H_kv, int N, int d, float scale, int causal, int dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
+  if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
   if (is_empty(B, H, N)) return FA2_OK;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
@@ -80,26 +90,41 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
   float* delta = static_cast<float*>(workspace);
   float* lse2 = delta + fa2::align256(rows * sizeof(float)) / sizeof(float);
-  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, delta, lse2,
+  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, H_kv, scale, causal != 0, dtype, delta, lse2,
                  static_cast<hipStream_t>(stream)};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }
 
+int fa2_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                    void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
 int fa2_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
-                       workspace_bytes, stream);
+  return fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, workspace,
+                         workspace_bytes, stream);
+}
+
+int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+                          float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
+  return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype,
+                       workspace, workspace_bytes, stream);
 }
 
 int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dO,
                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                        int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
-  return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
-                       workspace, workspace_bytes, stream);
+  return fa2_backward_stage_ex(stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, scale, causal, dtype,
+                               workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -120,7 +120,7 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int N,
-    int BH, float sl2, float scale) {
+    int BHkv, float sl2, float scale, int H, int G) {
   using C = DkdvTile<T, D>;
   constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB, QS = C::QS;
   // Double-buffered query-side tiles: one barrier per query tile.
@@ -133,13 +133,15 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / BH;  // ascending: for causal the heaviest key tiles go first
-  const int bh = lin % BH;
-  const size_t base = (size_t)bh * N * D;
-  const T* Qh = Q + base;
-  const T* dOh = dO + base;
-  const float* lseh = LSE + (size_t)bh * N;
-  const float* dlh = Delta + (size_t)bh * N;
+  const int kt = lin / BHkv;  // ascending: for causal the heaviest key tiles go first
+  const int bhk = lin % BHkv;  // key/value head; it serves query heads bh0 .. bh0 + G - 1
+  const int bh0 = (bhk / (H / G)) * H + (bhk % (H / G)) * G;
+  const size_t base = (size_t)bhk * N * D;
+  // Query-side pointers of the query head being walked (set per head below).
+  const T* Qh = Q;
+  const T* dOh = dO;
+  const float* lseh = LSE;
+  const float* dlh = Delta;
   const int kv0 = kt * BC;
   const int kw = kv0 + 32 * w;  // first key of this wave
   const int kj = kw + l32;      // key (accumulator column) owned by this lane
@@ -199,13 +201,6 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
       dl_s[buf][tid] = dr;
     }
   };
-
-  if (qt_begin < n_qt) {
-    load_q(qt_begin);
-    store_q(0);
-    if (qt_begin + 1 < n_qt) load_q(qt_begin + 1);
-  }
-  __syncthreads();
 
   // A buffer is rewritten (store_q) one tile after its last reads, and every
   // wave has passed the barrier that follows those reads by then.
@@ -306,11 +301,26 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     if (qt + 2 < n_qt) load_q(qt + 2);
   };
   // Query tiles that cross this key tile's diagonal band (or every tile when
-  // the key tile is ragged) run with the mask; the rest need none.
+  // the key tile is ragged) run with the mask; the rest need none.  The walk
+  // is repeated for each query head that shares these keys (grouped-query
+  // attention), accumulating into the same dK, dV.
   const int qt_mask_end = (kv0 + BC > N) ? n_qt : (CAUSAL ? min(n_qt, (kv0 + BC - 1) / BR + 1) : qt_begin);
-  int qt = qt_begin, it = 0;
-  for (; qt < qt_mask_end; ++qt, ++it) iteration(qt, it, BoolC<true>{});
-  for (; qt < n_qt; ++qt, ++it) iteration(qt, it, BoolC<false>{});
+  for (int g = 0; g < G; ++g) {
+    const int bh = bh0 + g;
+    Qh = Q + (size_t)bh * N * D;
+    dOh = dO + (size_t)bh * N * D;
+    lseh = LSE + (size_t)bh * N;
+    dlh = Delta + (size_t)bh * N;
+    if (qt_begin < n_qt) {
+      load_q(qt_begin);
+      store_q(0);
+      if (qt_begin + 1 < n_qt) load_q(qt_begin + 1);
+    }
+    __syncthreads();
+    int qt = qt_begin, it = 0;
+    for (; qt < qt_mask_end; ++qt, ++it) iteration(qt, it, BoolC<true>{});
+    for (; qt < n_qt; ++qt, ++it) iteration(qt, it, BoolC<false>{});
+  }
 
   if (kj < N) {
     T* dKj = dK + base + (size_t)kj * D;
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
                                                         const T* __restrict__ V, const T* __restrict__ dO,
                                                         const float* __restrict__ LSE,
                                                         const float* __restrict__ Delta, T* __restrict__ dQ, int N,
-                                                        int BH, int num_qt, float sl2, float scale) {
+                                                        int BH, int num_qt, float sl2, float scale, int H, int G) {
   using C = DqTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -373,8 +383,9 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
   const size_t base = (size_t)bh * N * D;
-  const T* Kh = K + base;
-  const T* Vh = V + base;
+  const size_t kv_base = (size_t)kv_head(bh, H, G) * N * D;
+  const T* Kh = K + kv_base;
+  const T* Vh = V + kv_base;
   const int q0 = qt * C::BR;
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
@@ -524,7 +535,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
                                                                const float* __restrict__ Lse2,
                                                                const float* __restrict__ Delta,
                                                                __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                                                               int N, int BH, float sl2, float scale) {
+                                                               int N, int BHkv, float sl2, float scale, int H,
+                                                               int G) {
   using namespace d128;
   typedef __bf16 T;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
@@ -536,19 +548,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / BH;  // ascending: for causal the heaviest key tiles go first
-  const int bh = lin % BH;
-  const size_t base = (size_t)bh * N * D;
-  const T* Qh = Q + base;
-  const T* dOh = dO + base;
+  const int kt = lin / BHkv;  // ascending: for causal the heaviest key tiles go first
+  const int bhk = lin % BHkv;  // key/value head; it serves query heads bh0 .. bh0 + G - 1
+  const int bh0 = (bhk / (H / G)) * H + (bhk % (H / G)) * G;
+  const size_t base = (size_t)bhk * N * D;
   const T* Vh = V + base;
-  const float* lseh = Lse2 + (size_t)bh * N;  // LSE * log2(e)
-  const float* dlh = Delta + (size_t)bh * N;
   const int kv0 = kt * BC;
   const int kw = kv0 + 32 * w;  // first key of this wave
   const int kj = kw + l32;      // key owned by this lane
-  const u32x4 rq = make_rsrc(Qh, (unsigned)N * D * 2);
-  const u32x4 rdo = make_rsrc(dOh, (unsigned)N * D * 2);
+  // Query-side sources of the query head being walked (set per head below):
+  // Q and dO as buffers, LSE * log2(e) and D.
+  u32x4 rq, rdo;
+  const float* lseh = Lse2;
+  const float* dlh = Delta;
 
   u32x4 kf[DCH];
   {
@@ -598,10 +610,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
       dload4(h ? dlh + i : lseh + i, &LD[buf][0]);
     }
   };
-
-  issue(0, 0);
-  wait_vmem();
-  __syncthreads();
 
   const SwzOffsets so = swz_offsets(lane);
   // One step: 32 query rows against this wave's 32 keys.
@@ -686,10 +694,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
   const int full_steps = N / BR - qt_begin;
   const int st_bulk_begin = (kv0 + BC > N) ? n_st : (CAUSAL ? min(n_st, BC / BR) : 0);
   const int st_bulk_end = max(st_bulk_begin, min(n_st, full_steps));
-  int st = 0;
-  for (; st < st_bulk_begin; ++st) step(st, BoolC<true>{});
-  for (; st < st_bulk_end; ++st) step(st, BoolC<false>{});
-  for (; st < n_st; ++st) step(st, BoolC<true>{});
+  // The walk is repeated for each query head that shares these keys
+  // (grouped-query attention), accumulating into the same dK, dV.
+  for (int g = 0; g < G; ++g) {
+    const int bh = bh0 + g;
+    rq = make_rsrc(Q + (size_t)bh * N * D, (unsigned)N * D * 2);
+    rdo = make_rsrc(dO + (size_t)bh * N * D, (unsigned)N * D * 2);
+    lseh = Lse2 + (size_t)bh * N;
+    dlh = Delta + (size_t)bh * N;
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    int st = 0;
+    for (; st < st_bulk_begin; ++st) step(st, BoolC<true>{});
+    for (; st < st_bulk_end; ++st) step(st, BoolC<false>{});
+    for (; st < n_st; ++st) step(st, BoolC<true>{});
+  }
 
   // Stage the bf16 results row-major in LDS (16-byte chunks swizzled like
   // the tiles): dK in the V tile, dV in the Q/dO buffers, both free now.
@@ -735,7 +755,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const __bf16* __res
                                                               const float* __restrict__ Lse2,
                                                               const float* __restrict__ Delta,
                                                               __bf16* __restrict__ dQ, int N, int BH, int num_qt,
-                                                              float sl2, float scale) {
+                                                              float sl2, float scale, int H, int G) {
   using namespace tiles;
   typedef __bf16 T;
   constexpr int D = 128, KB = 32, BLK_E = KB * 128, CH = 8, DCH = D / 16, NB = D / 32;
@@ -756,7 +776,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const __bf16* __res
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
   // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
   // q = 4w + u, rows 4(q%8)..+3 of the block.
-  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + base, (unsigned)N * D * 2);
+  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_head(bh, H, G) * N * D, (unsigned)N * D * 2);
   T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
 
   const int kv_end = CAUSAL ? min(N, q0 + QB) : N;
@@ -901,6 +921,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const __bf16* __res
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
+  const int BHkv = a.B * a.Hkv;  // dK/dV workgroups run over key/value heads
+  const int G = a.H / a.Hkv;     // query heads per key/value head
   const long long rows = (long long)BH * a.N;
   const float sl2 = a.scale * kLog2e;
   if (stage == 1) {
@@ -911,22 +933,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     return hipGetLastError();
   }
   if (stage == 2 && sizeof(T) == 2 && D == 128) {
-    const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BH;
+    const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BHkv;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_d128_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
-                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, sl2, a.scale);
+                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G);
     return hipGetLastError();
   }
   if (stage == 2) {
     using C = DkdvTile<T, D>;
-    const long long blocks = (long long)((a.N + C::BC - 1) / C::BC) * BH;
+    const long long blocks = (long long)((a.N + C::BC - 1) / C::BC) * BHkv;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
-                       a.N, BH, sl2, a.scale);
+                       a.N, BHkv, sl2, a.scale, a.H, G);
     return hipGetLastError();
   }
   if (stage == 3 && sizeof(T) == 2 && D == 128) {
@@ -936,7 +958,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_dq_d128_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
-                       static_cast<__bf16*>(a.dq), a.N, BH, num_qt, sl2, a.scale);
+                       static_cast<__bf16*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G);
     return hipGetLastError();
   }
   if (stage == 3) {
@@ -947,7 +969,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dq), a.N, BH, num_qt, sl2,
-                       a.scale);
+                       a.scale, a.H, G);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -196,6 +196,11 @@ __device__ __forceinline__ void write_transposed4<__bf16>(__bf16* tile, int row_
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Grouped-query attention: query head bh = b*H + h reads key/value head
+// (b, h / G) of the [B, H/G, N, d] key/value tensors (G = 1: plain
+// multi-head attention).  Returns that head's index b*(H/G) + h/G.
+__device__ __forceinline__ int kv_head(int bh, int H, int G) { return (bh / H) * (H / G) + (bh % H) / G; }
+
 // The value held by lane l ^ 32 (the other half of the wave), through the
 // gfx950 half-swap of two registers: a VALU operation, where a shuffle would
 // make a round trip through the LDS unit.  The swap exchanges the upper half

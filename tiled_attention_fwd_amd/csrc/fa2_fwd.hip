@@ -67,7 +67,7 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH, int num_qt,
-                                                     float sl2) {
+                                                     float sl2, int H, int G) {
   using C = FwdTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -79,9 +79,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
   const size_t base = (size_t)bh * N * D;
+  const size_t kv_base = (size_t)kv_head(bh, H, G) * N * D;
   const T* Qh = Q + base;
-  const T* Kh = K + base;
-  const T* Vh = V + base;
+  const T* Kh = K + kv_base;
+  const T* Vh = V + kv_base;
   const int q0 = qt * C::BR;
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
@@ -259,7 +260,7 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                         float* __restrict__ LSE, int N, int BH, int num_qt,
-                                                        float sl2) {
+                                                        float sl2, int H, int G) {
   using namespace tiles;
   typedef __bf16 T;
   constexpr int D = fpp::D, KB = fpp::KB, BLK_E = fpp::BLK_E;
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const __bf16* __restrict
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
   // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
   // q = 4w + u, rows 4(q%8)..+3 of the block.
-  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + base, (unsigned)N * D * 2);
+  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_head(bh, H, G) * N * D, (unsigned)N * D * 2);
   T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
 
   const int kv_end = CAUSAL ? min(N, q0 + fpp::BR) : N;
@@ -458,7 +459,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
     hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, BH, num_qt,
-                       a.scale * kLog2e);
+                       a.scale * kLog2e, a.H, a.H / a.Hkv);
     return hipGetLastError();
   }
   using C = FwdTile<T, D>;
@@ -469,7 +470,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   const float sl2 = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2);
+                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv);
   return hipGetLastError();
 }
 

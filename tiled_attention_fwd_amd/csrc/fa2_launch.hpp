@@ -19,6 +19,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, N, d;
+  int Hkv;  // key/value heads (divides H; H / Hkv query heads share one)
   float scale;
   bool causal;
   int dtype;
@@ -36,6 +37,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   int B, H, N, d;
+  int Hkv;  // key/value heads (divides H; H / Hkv query heads share one)
   float scale;
   bool causal;
   int dtype;

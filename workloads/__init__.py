@@ -16,7 +16,8 @@ Recipe (identical for every workload): a CPU ``torch.Generator`` seeded with
 the workload's seed draws ``torch.randn`` tensors of shape [B, H, N, d] in
 float32, in the order q, k, v, dO.  Where ``qk_mult`` is not 1 (a power of two,
 so exact), q and k are multiplied by it.  bf16 workloads then round every
-tensor to bfloat16 (round to nearest even).  The oracle receives the same
+tensor to bfloat16 (round to nearest even).  Grouped-query cases (``H_kv``
+key/value heads below H) draw k and v with shape [B, H_kv, N, d].  The oracle receives the same
 tensors converted to float64, so input rounding is never counted as error.
 """
 from __future__ import annotations
@@ -38,6 +39,11 @@ class Workload:
     causal: bool
     seed: int
     qk_mult: float = 1.0
+    H_kv: int = 0  # key/value heads; 0 means H (plain multi-head attention)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def scale(self) -> float:
@@ -51,9 +57,9 @@ class Workload:
         return (self.B, self.H, self.N, self.d)
 
     def describe(self) -> str:
-        return "%s B%d H%d N%d d%d %s %s" % (
-            self.name, self.B, self.H, self.N, self.d, self.dtype,
-            "causal" if self.causal else "non-causal")
+        return "%s B%d H%d%s N%d d%d %s %s" % (
+            self.name, self.B, self.H, "" if self.kv_heads == self.H else "/kv%d" % self.kv_heads, self.N,
+            self.d, self.dtype, "causal" if self.causal else "non-causal")
 
 
 WORKLOADS = {
@@ -70,9 +76,10 @@ def make_inputs(w: Workload, seed: int | None = None, device: str | torch.device
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else int(seed))
     shp = w.shape()
+    kv_shp = (w.B, w.kv_heads, w.N, w.d)
     q = torch.randn(shp, generator=g, dtype=torch.float32)
-    k = torch.randn(shp, generator=g, dtype=torch.float32)
-    v = torch.randn(shp, generator=g, dtype=torch.float32)
+    k = torch.randn(kv_shp, generator=g, dtype=torch.float32)
+    v = torch.randn(kv_shp, generator=g, dtype=torch.float32)
     dO = torch.randn(shp, generator=g, dtype=torch.float32)
     if w.qk_mult != 1.0:
         q = q * w.qk_mult
@@ -87,6 +94,6 @@ def make_inputs(w: Workload, seed: int | None = None, device: str | torch.device
 
 
 def custom(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
-           qk_mult: float = 1.0, name: str = "custom") -> Workload:
+           qk_mult: float = 1.0, name: str = "custom", H_kv: int = 0) -> Workload:
     """A workload outside the named five (edge-case shapes in the tests)."""
-    return Workload(name, B, H, N, d, dtype, causal, seed, qk_mult)
+    return Workload(name, B, H, N, d, dtype, causal, seed, qk_mult, H_kv)

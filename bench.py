@@ -17,7 +17,10 @@ kernel (its counted FLOP per launch over its mean event-timed duration,
 against the bf16 dense MFMA peak) and the oracle's CPU throughput on a
 bounded sample of heads of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 1..5]
+    python bench.py [--steps K] [--warmup W] [--workload 1..6]
+
+Workload 6 is the same shape with grouped-query attention (16 query heads
+over 2 key/value heads); its line is not the headline.
 """
 from __future__ import annotations
 
@@ -83,14 +86,16 @@ def stored_traffic(kernel: str, workload: str):
 def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
     """Time the fp64 oracle (test infrastructure) on whole heads of the same
     workload until about ``budget_s`` seconds of work are done; also report
-    the GPU's error on those heads."""
+    the GPU's error on those heads.  With grouped-query attention the unit is
+    a key/value head with its group of query heads (dK, dV are group sums)."""
     import numpy as np
     import oracle
 
     orc = oracle.default()
     q, k, v, dO = (t.cpu() for t in inputs)
     o, lse, dq, dk, dv = (t.float().cpu() for t in gpu_outs)
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    G = w.H // w.kv_heads
+    units = [(b, hk) for b in range(w.B) for hk in range(w.kv_heads)]
     done, t_total = 0, 0.0
     errs = {n: 0.0 for n in ("O", "LSE", "dQ", "dK", "dV")}
 
@@ -98,24 +103,26 @@ def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
         a = np.asarray(a, dtype=np.float64)
         return float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-300))
 
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
+    for b, hk in units:
+        sq = (slice(b, b + 1), slice(hk * G, (hk + 1) * G))
+        sk = (slice(b, b + 1), slice(hk, hk + 1))
         t0 = time.perf_counter()
-        o_r, lse_r = orc.fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
-        dq_r, dk_r, dv_r = orc.bwd(q[sl], k[sl], v[sl], dO[sl], w.scale, w.causal)
+        o_r, lse_r = orc.fwd(q[sq], k[sk], v[sk], w.scale, w.causal)
+        dq_r, dk_r, dv_r = orc.bwd(q[sq], k[sk], v[sk], dO[sq], w.scale, w.causal)
         t_total += time.perf_counter() - t0
         done += 1
-        for name, a, r in (("O", o[sl], o_r), ("LSE", lse[sl], lse_r), ("dQ", dq[sl], dq_r),
-                           ("dK", dk[sl], dk_r), ("dV", dv[sl], dv_r)):
+        for name, a, r in (("O", o[sq], o_r), ("LSE", lse[sq], lse_r), ("dQ", dq[sq], dq_r),
+                           ("dK", dk[sk], dk_r), ("dV", dv[sk], dv_r)):
             errs[name] = max(errs[name], rel(a, r))
         if t_total >= budget_s:
             break
-    step_flop_per_head = counted_flop(w)[2] / (w.B * w.H)
-    value = step_flop_per_head * done / t_total / 1e12
+    step_flop_per_unit = counted_flop(w)[2] / (w.B * w.kv_heads)
+    value = step_flop_per_unit * done / t_total / 1e12
+    what = "heads" if G == 1 else "key/value heads (x%d query heads)" % G
     return {
         "value": value, "unit": "TFLOP/s", "cores": orc.max_threads(), "kind": "oracle",
-        "sample": "%d of %d heads of %s, fp64 forward+backward, %.1f s" % (done, len(heads), w.name, t_total),
-    }, {"heads_checked": done, "max_rel_err": errs}
+        "sample": "%d of %d %s of %s, fp64 forward+backward, %.1f s" % (done, len(units), what, w.name, t_total),
+    }, {"units_checked": done, "max_rel_err": errs}
 
 
 def main() -> int:
@@ -157,18 +164,22 @@ def main() -> int:
     B, H, N, d = w.shape()
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(fa.fa2_backward_workspace_size(B, H, N, d, q.dtype), 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # Grouped-query workloads go through the entry points with a key/value
+    # head count; plain multi-head ones through the original calls.
+    fwd_call = fa.fa2_forward_ex if w.kv_heads != H else fa.fa2_forward
+    stage_call = fa.fa2_backward_stage_ex if w.kv_heads != H else fa.fa2_backward_stage
 
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        fa.fa2_forward(q, k, v, o, lse, w.causal, w.scale, stream)
+        fwd_call(q, k, v, o, lse, w.causal, w.scale, stream)
         for s in (1, 2, 3):
             if evs:
                 evs[s].record(stream)
-            fa.fa2_backward_stage(s, q, k, v, o, dO, lse, dq, dk, dv, w.causal, w.scale, ws, stream)
+            stage_call(s, q, k, v, o, dO, lse, dq, dk, dv, w.causal, w.scale, ws, stream)
         if evs:
             evs[4].record(stream)
 
@@ -211,7 +222,7 @@ def main() -> int:
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+        "config": {"workload": w.name, "B": B, "H": H, "H_kv": w.kv_heads, "N": N, "d": d, "causal": w.causal,
                    "seed": w.seed if args.seed is None else args.seed},
         "roofline": roofline,
     }

@@ -10,7 +10,8 @@ article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype Paved
 the Way for High-Performance WebGPU Flash Attention 2" (section "Memory
 Bandwidth Optimization") says is no longer moved per layer and step, the
 large bf16 causal case, and a ragged non-causal bf16 stress case whose Q and K
-are scaled by 8 so the online-softmax maximum is rescaled often.
+are scaled by 8 so the online-softmax maximum is rescaled often; a sixth is
+the large case with grouped-query attention (2 key/value heads).
 
 Recipe (identical for every workload): a CPU ``torch.Generator`` seeded with
 the workload's seed draws ``torch.randn`` tensors of shape [B, H, N, d] in
@@ -68,6 +69,9 @@ WORKLOADS = {
     3: Workload("mega_class_causal_f32", 8, 8, 512, 64, "f32", True, 3),
     4: Workload("large_causal_bf16", 4, 16, 4096, 128, "bf16", True, 4),
     5: Workload("ragged_noncausal_bf16", 16, 12, 1000, 64, "bf16", False, 5, 8.0),
+    # Grouped-query variant of workload 4: 16 query heads over 2 key/value
+    # heads (groups of 8).
+    6: Workload("large_causal_gqa_bf16", 4, 16, 4096, 128, "bf16", True, 6, 1.0, 2),
 }
 
 

@@ -165,7 +165,8 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(fa.fa2_backward_workspace_size(B, H, N, d, q.dtype), 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(fa.fa2_backward_workspace_size_ex(B, H, k.shape[1], N, d, q.dtype), 16),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     # Grouped-query workloads go through the entry points with a key/value
     # head count; plain multi-head ones through the original calls.

@@ -125,12 +125,19 @@ int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, c
  *   k, v   [B, H_kv, N, d]; dk, dv (backward) [B, H_kv, N, d], each the sum
  *          of the gradients of the group's query heads, written once
  *          (overwritten, never accumulated into).
- *   q, o, dO, dq [B, H, N, d] and lse [B, H, N] as before; the workspace
- *          size is fa2_backward_workspace_size(B, H, N, d, dtype).
- * The dK/dV kernel walks the query heads of a group in one workgroup per
- * key tile, so no atomics are used and results are the same bits from run
- * to run.
+ *   q, o, dO, dq [B, H, N, d] and lse [B, H, N] as before.
+ *   workspace  at least fa2_backward_workspace_size_ex(B, H, H_kv, N, d,
+ *          dtype) bytes (which equals fa2_backward_workspace_size when
+ *          H_kv = H).
+ * The dK/dV kernel walks the query heads of a group inside one workgroup
+ * per key tile.  When that leaves too few workgroups to fill the device
+ * (bf16, d = 128), each group is split over S workgroups (S divides G) that
+ * write fp32 partial sums into the workspace, and a second kernel of stage
+ * 2 adds the S partials in a fixed order and rounds once.  No atomics either
+ * way, so results are the same bits from run to run.
  */
+size_t fa2_backward_workspace_size_ex(int B, int H, int H_kv, int N, int d, int dtype);
+
 int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
                    void* stream);

@@ -33,7 +33,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert names == ["fa2_backward", "fa2_backward_ex", "fa2_backward_stage", "fa2_backward_stage_ex",
-                     "fa2_backward_workspace_size", "fa2_forward", "fa2_forward_ex", "fa2_status_string"]
+                     "fa2_backward_workspace_size", "fa2_backward_workspace_size_ex", "fa2_forward",
+                     "fa2_forward_ex", "fa2_status_string"]
     for n in names:
         assert hasattr(L, n), n
 
@@ -104,6 +105,40 @@ def test_workspace_size_formula(L):
     assert L.fa2_backward_workspace_size(-1, H, N, d, 1) == 0
 
 
+def test_workspace_size_ex_formula(L):
+    """Grouped-query sizes: the plain size, plus fp32 partial dK and dV when a
+    bf16 d=128 group is split over S workgroups (S the smallest divisor of G
+    giving 1024 key-tile workgroups, else G)."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    B, H, N, d = 4, 16, 4096, 128
+    plain = 2 * al(B * H * N * 4)
+    assert L.fa2_backward_workspace_size_ex(B, H, H, N, d, 1) == L.fa2_backward_workspace_size(B, H, N, d, 1)
+    # 32 key tiles x 4 x 2 = 256 workgroups -> S = 4 of G = 8
+    assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 1) == plain + 2 * al(4 * B * 2 * N * d * 4)
+    # 32 x 4 x 1 = 128 -> S = 8 of G = 16
+    assert L.fa2_backward_workspace_size_ex(B, H, 1, N, d, 1) == plain + 2 * al(8 * B * 1 * N * d * 4)
+    # tiny problem: S = G
+    assert L.fa2_backward_workspace_size_ex(1, 8, 1, 64, 128, 1) == 2 * al(8 * 64 * 4) + 2 * al(8 * 64 * 128 * 4)
+    # G = 6 with 1 key tile: S runs 2, 3, 6
+    assert L.fa2_backward_workspace_size_ex(1, 6, 1, 64, 128, 1) == 2 * al(6 * 64 * 4) + 2 * al(6 * 64 * 128 * 4)
+    # enough workgroups already (16 x 8 x 8 = 1024), fp32, or another head size: no partials
+    assert L.fa2_backward_workspace_size_ex(8, 16, 8, 2048, d, 1) == 2 * al(8 * 16 * 2048 * 4)
+    assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 0) == plain
+    assert L.fa2_backward_workspace_size_ex(B, H, 2, N, 64, 1) == plain
+    assert L.fa2_backward_workspace_size_ex(B, H, 3, N, d, 1) == 0
+    assert L.fa2_backward_workspace_size_ex(0, H, 2, N, d, 1) == 0
+
+
+def test_backward_ex_wants_the_ex_workspace(L):
+    need = L.fa2_backward_workspace_size_ex(1, 8, 1, 64, 128, 1)
+    short = L.fa2_backward_workspace_size(1, 8, 64, 128, 1)
+    assert need > short
+    args = (A,) * 9 + (1, 8, 1, 64, 128, 0.125, 1, 1, A)
+    assert L.fa2_backward_ex(*args, short, None) == fa.FA2_ERR_WORKSPACE
+    assert L.fa2_backward_stage_ex(2, *args, need - 1, None) == fa.FA2_ERR_WORKSPACE
+
+
 def test_status_strings(L):
     for s in range(5):
         txt = L.fa2_status_string(s).decode()
@@ -143,7 +178,7 @@ def fwd_ex(L, H=4, H_kv=2, ptr=A, **over):
 
 
 def bwd_ex(L, H=4, H_kv=2, ptr=A, stage=None):
-    wsb = L.fa2_backward_workspace_size(1, H, 64, 64, 1)
+    wsb = L.fa2_backward_workspace_size_ex(1, H, max(H_kv, 1), 64, 64, 1)
     args = (ptr,) * 9 + (1, H, H_kv, 64, 64, 0.125, 1, 1, A, wsb, None)
     if stage is None:
         return L.fa2_backward_ex(*args)

@@ -76,22 +76,26 @@ def gpu_fwd_bwd(q, k, v, dO, causal, scale):
 
 
 def check_against_oracle(w, q, k, v, dO, outs, heads=None):
-    """Compare GPU outputs with the oracle, on all heads or on (b, h) pairs."""
+    """Compare GPU outputs with the oracle, on all heads or on (b, h) pairs.
+
+    With grouped-query inputs h names a key/value head, and the comparison
+    covers it together with every query head of its group."""
     o, lse, dq, dk, dv = (t.float().cpu() for t in outs)
     qc, kc, vc, gc = (t.cpu() for t in (q, k, v, dO))
+    G = q.shape[1] // k.shape[1]
     if heads is None:
-        sel = [(slice(None), slice(None))]
+        sel = [(slice(None), slice(None), slice(None))]
     else:
-        sel = [(slice(b, b + 1), slice(h, h + 1)) for b, h in heads]
+        sel = [(slice(b, b + 1), slice(h * G, (h + 1) * G), slice(h, h + 1)) for b, h in heads]
     errs = {n: 0.0 for n in ("O", "LSE", "dQ", "dK", "dV")}
-    for bs, hs in sel:
-        o_r, lse_r = oracle.fwd(qc[bs, hs], kc[bs, hs], vc[bs, hs], w.scale, w.causal)
-        dq_r, dk_r, dv_r = oracle.bwd(qc[bs, hs], kc[bs, hs], vc[bs, hs], gc[bs, hs], w.scale, w.causal)
+    for bs, hs, ks in sel:
+        o_r, lse_r = oracle.fwd(qc[bs, hs], kc[bs, ks], vc[bs, ks], w.scale, w.causal)
+        dq_r, dk_r, dv_r = oracle.bwd(qc[bs, hs], kc[bs, ks], vc[bs, ks], gc[bs, hs], w.scale, w.causal)
         errs["O"] = max(errs["O"], rel_err(o[bs, hs], o_r))
         errs["LSE"] = max(errs["LSE"], rel_err(lse[bs, hs], lse_r))
         errs["dQ"] = max(errs["dQ"], rel_err(dq[bs, hs], dq_r))
-        errs["dK"] = max(errs["dK"], rel_err(dk[bs, hs], dk_r))
-        errs["dV"] = max(errs["dV"], rel_err(dv[bs, hs], dv_r))
+        errs["dK"] = max(errs["dK"], rel_err(dk[bs, ks], dk_r))
+        errs["dV"] = max(errs["dV"], rel_err(dv[bs, ks], dv_r))
     return errs
 
 
@@ -234,6 +238,22 @@ def test_mqa_long_bf16():
     """Multi-query attention at the large workload's head size and a long,
     ragged sequence: 8 query heads on one K, V head."""
     run_case(workloads.custom(1, 8, 2049, 128, "bf16", True, 3101, name="mqa", H_kv=1))
+
+
+def test_gqa_bench_workload_sampled_heads():
+    """The grouped-query workload at full size (4 x 16 query heads over 2
+    key/value heads, N = 4096, d = 128, causal bf16), as the benchmark runs
+    it: its dK/dV stage splits each group of 8 over 4 workgroups of 2 heads
+    and sums the partials.  Two key/value heads, with their 8 query heads
+    each, against the oracle."""
+    run_case(workloads.WORKLOADS[6], heads=[(0, 0), (3, 1)])
+
+
+def test_gqa_unsplit_sampled_heads():
+    """Enough key tiles (16 x 8 x 8 = 1024 workgroups) that the dK/dV kernel
+    keeps each group of 2 query heads in one workgroup."""
+    run_case(workloads.custom(8, 16, 2048, 128, "bf16", True, 3103, name="gqa", H_kv=8),
+             heads=[(0, 0), (5, 3), (7, 7)])
 
 
 def test_gqa_backward_bitwise_repeatable():

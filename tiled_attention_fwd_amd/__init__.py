@@ -7,7 +7,7 @@ library is not built, importing works but every call raises ``Fa2Error``.
 
 Functions with the C names (``fa2_forward``, ``fa2_backward``,
 ``fa2_backward_stage``, their ``_ex`` forms with a key/value head count for
-grouped-query attention, ``fa2_backward_workspace_size``,
+grouped-query attention, ``fa2_backward_workspace_size`` (``_ex``),
 ``fa2_status_string``) take caller-allocated tensors like the C ABI;
 ``forward`` / ``backward`` allocate the outputs (K and V may have fewer heads
 than Q: H_kv dividing H).
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.fa2_backward_stage_ex.restype = i
         L.fa2_backward_workspace_size.argtypes = [i, i, i, i, i]
         L.fa2_backward_workspace_size.restype = ctypes.c_size_t
+        L.fa2_backward_workspace_size_ex.argtypes = [i, i, i, i, i, i]
+        L.fa2_backward_workspace_size_ex.restype = ctypes.c_size_t
         L.fa2_status_string.argtypes = [i]
         L.fa2_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -155,6 +157,11 @@ def fa2_backward_workspace_size(B: int, H: int, N: int, d: int, dtype) -> int:
     return int(lib().fa2_backward_workspace_size(B, H, N, d, code))
 
 
+def fa2_backward_workspace_size_ex(B: int, H: int, H_kv: int, N: int, d: int, dtype) -> int:
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().fa2_backward_workspace_size_ex(B, H, H_kv, N, d, code))
+
+
 def fa2_backward(q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True, scale: float | None = None,
                  workspace: torch.Tensor | None = None, stream=None) -> None:
     """Enqueue the backward pass into caller-allocated ``dq``, ``dk``, ``dv``."""
@@ -194,7 +201,7 @@ def _backward_call(ex, stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, wo
         raise ValueError("fa2_backward needs H_kv == H; use fa2_backward_ex")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, H, N]")
-    need = fa2_backward_workspace_size(B, H, N, d, q.dtype)
+    need = fa2_backward_workspace_size_ex(B, H, H_kv, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),

@@ -66,10 +66,15 @@ int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse
   return fa2_forward_ex(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
 }
 
-size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
-  if (check_sizes(B, H, N, d, dtype) != FA2_OK) return 0;
+size_t fa2_backward_workspace_size_ex(int B, int H, int H_kv, int N, int d, int dtype) {
+  if (check_sizes(B, H, N, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
   if (is_empty(B, H, N)) return 0;
-  return fa2::ws_total_bytes((size_t)B * H * N, d, dtype);
+  const int S = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
+  return fa2::ws_total_bytes((size_t)B * H * N, d, dtype) + fa2::ws_part_bytes(B, H_kv, N, d, S);
+}
+
+size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
+  return fa2_backward_workspace_size_ex(B, H, H, N, d, dtype);
 }
 
 static int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v,
@@ -86,11 +91,16 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA2_ERR_UNSUPPORTED;
   const size_t rows = (size_t)B * H * N;
-  if (!workspace || workspace_bytes < fa2::ws_total_bytes(rows, d, dtype)) return FA2_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < fa2_backward_workspace_size_ex(B, H, H_kv, N, d, dtype))
+    return FA2_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
   float* delta = static_cast<float*>(workspace);
   float* lse2 = delta + fa2::align256(rows * sizeof(float)) / sizeof(float);
-  fa2::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, H_kv, scale, causal != 0, dtype, delta, lse2,
+  float* part = static_cast<float*>(static_cast<void*>(static_cast<char*>(workspace) +
+                                                       fa2::ws_total_bytes(rows, d, dtype)));
+  const int splits = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
+  fa2::BwdArgs a{q,  k, v, o,     dO,          lse,   dq,    dk,   dv,     B,     H,
+                 N,  d, H_kv, scale, causal != 0, dtype, delta, lse2, part, splits,
                  static_cast<hipStream_t>(stream)};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;

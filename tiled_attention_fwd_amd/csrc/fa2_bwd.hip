@@ -536,7 +536,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
                                                                const float* __restrict__ Delta,
                                                                __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                                                                int N, int BHkv, float sl2, float scale, int H,
-                                                               int G) {
+                                                               int G, int S, float* __restrict__ PartK,
+                                                               float* __restrict__ PartV) {
   using namespace d128;
   typedef __bf16 T;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
@@ -548,9 +549,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / BHkv;  // ascending: for causal the heaviest key tiles go first
+  const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
+  const int sp = (lin % (BHkv * S)) / BHkv;  // which 1/S of the group's query heads
   const int bhk = lin % BHkv;  // key/value head; it serves query heads bh0 .. bh0 + G - 1
-  const int bh0 = (bhk / (H / G)) * H + (bhk % (H / G)) * G;
+  const int gpw = G / S;       // query heads walked by this workgroup
+  const int bh0 = (bhk / (H / G)) * H + (bhk % (H / G)) * G + sp * gpw;
   const size_t base = (size_t)bhk * N * D;
   const T* Vh = V + base;
   const int kv0 = kt * BC;
@@ -696,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
   const int st_bulk_end = max(st_bulk_begin, min(n_st, full_steps));
   // The walk is repeated for each query head that shares these keys
   // (grouped-query attention), accumulating into the same dK, dV.
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < gpw; ++g) {
     const int bh = bh0 + g;
     rq = make_rsrc(Q + (size_t)bh * N * D, (unsigned)N * D * 2);
     rdo = make_rsrc(dO + (size_t)bh * N * D, (unsigned)N * D * 2);
@@ -711,6 +714,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
     for (; st < n_st; ++st) step(st, BoolC<true>{});
   }
 
+  if (S > 1) {
+    // One of S partial sums over the group: fp32 rows of [S][B, Hkv, N, d],
+    // dK already scaled; bwd_dkdv_reduce_kernel adds them up.
+    if (kj < N) {
+      const size_t row = ((size_t)sp * BHkv + bhk) * N + kj;
+      float* pk = PartK + row * D;
+      float* pv = PartV + row * D;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * b + 8 * g + 4 * h;
+          *reinterpret_cast<f32x4*>(pk + d0) = f32x4{dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale,
+                                                      dk[b][4 * g + 2] * scale, dk[b][4 * g + 3] * scale};
+          *reinterpret_cast<f32x4*>(pv + d0) = f32x4{dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2],
+                                                      dv[b][4 * g + 3]};
+        }
+      }
+    }
+    return;
+  }
   // Stage the bf16 results row-major in LDS (16-byte chunks swizzled like
   // the tiles): dK in the V tile, dV in the Q/dO buffers, both free now.
   T* sk = Vs;
@@ -918,6 +942,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const __bf16* __res
   }
 }
 
+// Sums of the S partial dK (blockIdx.y = 0) and dV (1) of a split
+// grouped-query dK/dV stage, in the fixed order s = 0 .. S-1, rounded once
+// to the output type: 4 elements per thread; n (elements per tensor) is a
+// multiple of 4 since d is.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ PartK,
+                                                              const float* __restrict__ PartV, T* __restrict__ dK,
+                                                              T* __restrict__ dV, long long n, int S) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const float* Part = blockIdx.y ? PartV : PartK;
+  T* Out = blockIdx.y ? dV : dK;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(Part + i);
+  for (int sp = 1; sp < S; ++sp) acc += *reinterpret_cast<const f32x4*>(Part + (size_t)sp * n + i);
+  store4<T>(Out + i, acc[0], acc[1], acc[2], acc[3]);
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
@@ -934,11 +975,21 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   }
   if (stage == 2 && sizeof(T) == 2 && D == 128) {
     const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BHkv;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_d128_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    if (blocks * a.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int S = a.splits;
+    const long long n = (long long)BHkv * a.N * D;  // elements of dK (and of dV)
+    float* part_k = a.part;
+    float* part_v = a.part + align256((size_t)S * n * sizeof(float)) / sizeof(float);
+    hipLaunchKernelGGL((bwd_dkdv_d128_kernel<CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
-                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G);
+                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G,
+                       S, part_k, part_v);
+    if (S > 1) {
+      const unsigned rb = (unsigned)((n / 4 + 255) / 256);
+      hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<__bf16>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,
+                         static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), n, S);
+    }
     return hipGetLastError();
   }
   if (stage == 2) {

@@ -53,6 +53,8 @@ class Oracle:
         lib.oracle_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, L,
                                        ctypes.c_double, ctypes.c_int]
         lib.oracle_bwd_f64.restype = ctypes.c_int
+        lib.oracle_decode_f64.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double, ctypes.c_int]
+        lib.oracle_decode_f64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -99,6 +101,24 @@ class Oracle:
             return dq, dk, dv, delta
         return dq, dk, dv
 
+    def decode(self, q, k, v, scale: float, causal: bool):
+        """Return (O, LSE) in fp64 for N_q queries q [B, H, N_q, d] against a
+        cache k, v [B, H_kv, N_k, d] (H_kv divides H); causal places the
+        queries at the last N_q positions (see oracle_decode_f64)."""
+        q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+        B, H, Nq, d = _shape(q)
+        k, v = _expand_kv(k, H), _expand_kv(v, H)
+        Nk = k.shape[2]
+        if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+            raise ValueError("k, v must be [B, H_kv, N_k, d] with q's B and d")
+        o = np.empty_like(q)
+        lse = np.empty((B, H, Nq), dtype=np.float64)
+        rc = self.lib.oracle_decode_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        B, H, Nq, Nk, d, float(scale), int(bool(causal)))
+        if rc != 0:
+            raise RuntimeError("oracle_decode_f64 failed with code %d" % rc)
+        return o, lse
+
 
 _default = None
 
@@ -118,6 +138,11 @@ def fwd(q, k, v, scale: float, causal: bool):
 def bwd(q, k, v, dO, scale: float, causal: bool, return_delta: bool = False):
     """(dQ, dK, dV[, D]) from the default oracle library."""
     return default().bwd(q, k, v, dO, scale, causal, return_delta)
+
+
+def decode(q, k, v, scale: float, causal: bool):
+    """(O, LSE) of N_q queries against an N_k cache, from the default oracle."""
+    return default().decode(q, k, v, scale, causal)
 
 
 def _expand_kv(t: np.ndarray, H: int) -> np.ndarray:

@@ -204,3 +204,69 @@ int oracle_bwd_f64(const double* q, const double* k, const double* v,
   free(P); free(dS); free(lse); free(D);
   return 0;
 }
+
+/*
+ * Decoding: N_q new queries against a cache of N_k keys and values.  The
+ * article names flash-decoding as a next primitive (section "Next Frontiers
+ * in WebGPU ML", "Broader Opset Support") without defining it; it is read as
+ * the same softmax attention with a rectangular score matrix,
+ *
+ *   S_ij  = scale * sum_k q_ik k_jk,  i < N_q, j < N_k
+ *   LSE_i = m_i + ln sum_j exp(S_ij - m_i),  P_ij = exp(S_ij - LSE_i)
+ *   O_i   = sum_j P_ij v_j
+ *
+ * where the queries are the last N_q positions of the sequence: with the
+ * causal mask, query i sits at position N_k - N_q + i and keeps keys
+ * j <= N_k - N_q + i (for N_q = N_k this is the mask of oracle_fwd_f64).
+ * Splitting the cache over workgroups and merging their partial results is
+ * how the fast path evaluates this; the oracle evaluates the definition.
+ *
+ * q, o: [B, H, N_q, d]; k, v: [B, H, N_k, d] (one key/value head per query
+ * head: grouped heads are expanded by the caller); lse: [B, H, N_q].
+ * Requires N_q <= N_k when causal and N_k >= 1 when N_q >= 1.
+ */
+int oracle_decode_f64(const double* q, const double* k, const double* v,
+                      double* o, double* lse, long B, long H, long Nq, long Nk,
+                      long d, double scale, int causal) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0) return 1;
+  if (B == 0 || H == 0 || Nq == 0) return 0;
+  if (Nk == 0 || (causal && Nq > Nk)) return 1;
+  const long off = Nk - Nq; /* position of query 0 in the sequence */
+  for (long bh = 0; bh < B * H; ++bh) {
+    const double* qh = q + bh * Nq * d;
+    const double* kh = k + bh * Nk * d;
+    const double* vh = v + bh * Nk * d;
+    double* oh = o + bh * Nq * d;
+    double* lh = lse + bh * Nq;
+    long i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < Nq; ++i) {
+      double* S = (double*)malloc(sizeof(double) * (size_t)Nk);
+      if (!S) { lh[i] = NAN; continue; }
+      const long last = causal ? off + i : Nk - 1; /* last visible key */
+      double m = -INFINITY;
+      for (long j = 0; j < Nk; ++j) {
+        if (j > last) {
+          S[j] = -INFINITY;
+          continue;
+        }
+        double acc = 0.0;
+        for (long c = 0; c < d; ++c) acc += qh[i * d + c] * kh[j * d + c];
+        S[j] = scale * acc;
+        if (S[j] > m) m = S[j];
+      }
+      double sum = 0.0;
+      for (long j = 0; j < Nk; ++j) sum += exp(S[j] - m);
+      const double L = m + log(sum);
+      lh[i] = L;
+      double* orow = oh + i * d;
+      for (long c = 0; c < d; ++c) orow[c] = 0.0;
+      for (long j = 0; j < Nk; ++j) {
+        const double p = exp(S[j] - L);
+        for (long c = 0; c < d; ++c) orow[c] += p * vh[j * d + c];
+      }
+      free(S);
+    }
+  }
+  return 0;
+}

@@ -287,6 +287,86 @@ def pin_gqa_shared_heads(orc, seed=48, H=3, N=9, d=4):
     assert rel_err(dk, H * dk1) < 1e-13 and rel_err(dv, H * dv1) < 1e-13
 
 
+# --------------------------------------------------------------------------
+# decoding: N_q new queries against an N_k cache (the article's "Next
+# Frontiers in WebGPU ML", "Broader Opset Support", names flash-decoding);
+# causal places the queries at the last N_q positions of the sequence
+# --------------------------------------------------------------------------
+def torch_decode_reference(q, k, v, scale, causal):
+    """(O, LSE) from torch float64 SDPA with an explicit boolean mask that
+    keeps key j for query i when j <= N_k - N_q + i."""
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    Nq, Nk = qt.shape[2], kt.shape[2]
+    gqa = kt.shape[1] != qt.shape[1]
+    mask = None
+    if causal:
+        i = torch.arange(Nq).unsqueeze(1)
+        j = torch.arange(Nk).unsqueeze(0)
+        mask = j <= i + (Nk - Nq)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=gqa)
+    kx = kt.repeat_interleave(qt.shape[1] // kt.shape[1], dim=1) if gqa else kt
+    logits = scale * torch.matmul(qt, kx.transpose(-1, -2).contiguous())
+    if causal:
+        logits = logits.masked_fill(~mask, float("-inf"))
+    return o.numpy(), torch.logsumexp(logits, dim=-1).numpy()
+
+
+def pin_decode_torch(orc):
+    """Single query, a few queries (causal and not) and grouped heads against
+    torch float64 SDPA with the bottom-right mask written out."""
+    for (B, H, Hkv, Nq, Nk, d, causal, sd) in [(1, 2, 2, 1, 37, 8, True, 50), (2, 2, 2, 5, 40, 8, True, 51),
+                                               (1, 3, 3, 7, 23, 4, False, 52), (2, 4, 2, 3, 29, 8, True, 53),
+                                               (1, 4, 1, 16, 16, 8, True, 54)]:
+        q = randn((B, H, Nq, d), sd)
+        k, v = randn((B, Hkv, Nk, d), sd + 100), randn((B, Hkv, Nk, d), sd + 200)
+        o, lse = orc.decode(q, k, v, 0.45, causal)
+        o_t, lse_t = torch_decode_reference(q, k, v, 0.45, causal)
+        assert rel_err(o, o_t) < 1e-12, ("O", Nq, Nk, causal)
+        assert rel_err(lse, lse_t) < 1e-12, ("LSE", Nq, Nk, causal)
+
+
+def pin_decode_suffix(orc, seed=55, N=24, Nq=6, d=4):
+    """The last N_q rows of causal attention over a whole sequence are the
+    decode of those N_q queries against the sequence's keys."""
+    q, k, v = randn((1, 2, N, d), seed), randn((1, 2, N, d), seed + 1), randn((1, 2, N, d), seed + 2)
+    o_full, lse_full = orc.fwd(q, k, v, 0.5, True)
+    o, lse = orc.decode(q[:, :, N - Nq:], k, v, 0.5, True)
+    assert rel_err(o, o_full[:, :, N - Nq:]) < 1e-13
+    assert rel_err(lse, lse_full[:, :, N - Nq:]) < 1e-13
+
+
+def pin_decode_merge(orc, seed=56, Nq=3, Nk=31, cut=12, d=5):
+    """Attention over a cache split in two parts equals the LSE-weighted
+    merge of the attention over each part (the identity split-KV decoding
+    rests on): O = (e^L1 O1 + e^L2 O2) / (e^L1 + e^L2), LSE = log(e^L1 + e^L2)."""
+    q = randn((1, 2, Nq, d), seed)
+    k, v = randn((1, 2, Nk, d), seed + 1), randn((1, 2, Nk, d), seed + 2)
+    o, lse = orc.decode(q, k, v, 0.6, False)
+    o1, l1 = orc.decode(q, k[:, :, :cut], v[:, :, :cut], 0.6, False)
+    o2, l2 = orc.decode(q, k[:, :, cut:], v[:, :, cut:], 0.6, False)
+    lm = np.logaddexp(l1, l2)
+    w1, w2 = np.exp(l1 - lm)[..., None], np.exp(l2 - lm)[..., None]
+    assert rel_err(lse, lm) < 1e-13
+    assert rel_err(o, w1 * o1 + w2 * o2) < 1e-13
+
+
+def pin_decode_q_zero(orc, seed=57, Nq=4, Nk=10, d=3):
+    """Q = 0: uniform weights over the visible keys, N_k - N_q + i + 1 of them
+    for causal query i (all N_k otherwise)."""
+    v = randn((1, 1, Nk, d), seed)
+    k = randn((1, 1, Nk, d), seed + 1)
+    q = np.zeros((1, 1, Nq, d))
+    for causal in (True, False):
+        o, lse = orc.decode(q, k, v, 0.7, causal)
+        for i in range(Nq):
+            n = Nk - Nq + i + 1 if causal else Nk
+            assert np.allclose(o[0, 0, i], v[0, 0, :n].mean(axis=0), rtol=0, atol=1e-14)
+            assert abs(lse[0, 0, i] - math.log(n)) < 1e-14
+    o1, l1 = orc.decode(randn((1, 1, 1, d), seed + 2), k, v, 0.7, True)
+    o2, l2 = orc.decode(randn((1, 1, 1, d), seed + 2), k, v, 0.7, False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)  # one query sees the whole cache
+
+
 ALL_SMALL_PINS = [
     pin_uniform_v, pin_direct_lse, pin_causal_row0, pin_q_zero, pin_single_key, pin_two_keys,
     pin_invariants, pin_permutation,
@@ -295,4 +375,5 @@ ALL_SMALL_PINS = [
     lambda orc: pin_torch(orc, *(randn((1, 2, 33, 8), 20 + t) for t in range(4)), 0.35, True),
     lambda orc: pin_torch(orc, *(randn((1, 2, 33, 8), 30 + t) for t in range(4)), 0.35, False),
     pin_gqa_torch, pin_gqa_shared_heads,
+    pin_decode_torch, pin_decode_suffix, pin_decode_merge, pin_decode_q_zero,
 ]

@@ -34,6 +34,15 @@ MUTATIONS = {
     "dk_uses_p": ("krow[c] += s * qh[ii * d + c];", "krow[c] += p * qh[ii * d + c];"),
     "dv_transposed_p": ("double p = P[ii * N + j], s", "double p = P[j * N + ii], s"),
     "dv_uses_q": ("vrow[c] += p * gh[ii * d + c];", "vrow[c] += p * qh[ii * d + c];"),
+    "decode_top_left_mask": ("const long last = causal ? off + i : Nk - 1;",
+                             "const long last = causal ? i : Nk - 1;"),
+    "decode_mask_off_by_one": ("const long last = causal ? off + i : Nk - 1;",
+                               "const long last = causal ? off + i - 1 : Nk - 1;"),
+    "decode_drop_scale": ("S[j] = scale * acc;", "S[j] = acc;"),
+    "decode_lse_drop_max": ("const double L = m + log(sum);", "const double L = log(sum);"),
+    "decode_p_unnormalised": ("const double p = exp(S[j] - L);", "const double p = exp(S[j] - m);"),
+    "decode_v_row_shift": ("orow[c] += p * vh[j * d + c];\n      }\n      free(S);",
+                           "orow[c] += p * vh[((j + 1) % Nk) * d + c];\n      }\n      free(S);"),
 }
 
 

@@ -18,9 +18,15 @@ against the bf16 dense MFMA peak) and the oracle's CPU throughput on a
 bounded sample of heads of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 1..6]
+    python bench.py --decode decode_gqa_bf16
 
 Workload 6 is the same shape with grouped-query attention (16 query heads
-over 2 key/value heads); its line is not the headline.
+over 2 key/value heads); its line is not the headline.  ``--decode`` times
+decoding instead (one new query per sequence against a 16 K cache, 64 query
+heads over 8 key/value heads): one step is one ``fa2_decode`` call (the
+split-cache kernel and the merge kernel); it is bound by HBM, so its line
+reports GB/s of algorithmic bytes (the cache read once, Q read, O and LSE
+written) against the 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -57,6 +63,7 @@ KERNEL_SOURCES = {
     "bwd_pre_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
     "bwd_dkdv_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
     "bwd_dq_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
+    "decode_kernel": ["fa2_decode.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
 }
 
 
@@ -125,6 +132,108 @@ def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
     }, {"units_checked": done, "max_rel_err": errs}
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decoding pass: K and V read once, Q read,
+    O and LSE written."""
+    s = 2 if w.dtype == "bf16" else 4
+    return 2 * w.B * w.H_kv * w.N_k * w.d * s + 2 * w.B * w.H * w.N_q * w.d * s + 4 * w.B * w.H * w.N_q
+
+
+def decode_cpu_baseline(w, inputs, gpu_outs, budget_s: float):
+    """The oracle's decode (test infrastructure) on whole key/value heads of
+    the same workload, each with its group of query heads, until about
+    ``budget_s`` seconds; GB/s of the same algorithmic bytes per unit."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.default()
+    q, k, v = (t.cpu() for t in inputs)
+    o, lse = (t.float().cpu() for t in gpu_outs)
+    G = w.H // w.H_kv
+    units = [(b, hk) for b in range(w.B) for hk in range(w.H_kv)]
+    done, t_total, err = 0, 0.0, 0.0
+    for b, hk in units:
+        sq = (slice(b, b + 1), slice(hk * G, (hk + 1) * G))
+        sk = (slice(b, b + 1), slice(hk, hk + 1))
+        t0 = time.perf_counter()
+        o_r, lse_r = orc.decode(q[sq], k[sk], v[sk], w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        for a, r in ((o[sq], o_r), (lse[sq], lse_r)):
+            a = np.asarray(a, dtype=np.float64)
+            err = max(err, float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-300)))
+        if t_total >= budget_s:
+            break
+    per_unit = decode_bytes(w) / len(units)
+    return {
+        "value": per_unit * done / t_total / 1e9, "unit": "GB/s", "cores": orc.max_threads(), "kind": "oracle",
+        "sample": "%d of %d key/value heads (x%d query heads) of %s, fp64 decode, %.1f s"
+                  % (done, len(units), G, w.name, t_total),
+    }, {"units_checked": done, "max_rel_err": err}
+
+
+def bench_decode(args) -> int:
+    import torch
+    import tiled_attention_fwd_amd as fa
+    import workloads
+
+    w = workloads.DECODE_WORKLOADS[args.decode]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = workloads.make_decode_inputs(w, seed=args.seed, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+    need = fa.fa2_decode_workspace_size(w.B, w.H, w.H_kv, w.N_q, w.N_k, w.d, q.dtype)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa2_decode(q, k, v, o, lse, w.causal, w.scale, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(K):
+        step()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    launch_ms = statistics.fmean(ev[s].elapsed_time(ev[s + 1]) for s in range(K))
+    nbytes = decode_bytes(w)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": "attention decode GB/s of algorithmic HBM bytes (bf16 B16 H64/kv8 Nq1 Nk16384 d128)",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
+                   "causal": w.causal, "seed": w.seed if args.seed is None else args.seed},
+        # One fa2_decode call is the decode kernel plus the small merge kernel;
+        # the events time both, so the kernel's own rate is a little higher.
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": achieved, "peak": HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_GBS, "traffic": stored_traffic("decode_kernel", w.name),
+                     "mean_launch_ms": launch_ms, "bytes_per_launch": nbytes},
+    }
+    detail = {"call_ms": launch_ms, "tflops": 4.0 * w.B * w.H * w.N_q * w.N_k * w.d / (launch_ms * 1e-3) / 1e12,
+              "workspace_bytes": need}
+    if args.cpu_budget > 0:
+        cb, parity = decode_cpu_baseline(w, (q, k, v), (o, lse), args.cpu_budget)
+        result["cpu_baseline"] = cb
+        detail["parity_sampled_heads"] = parity
+    else:
+        result["cpu_baseline"] = None
+    result["detail"] = detail
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +242,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--decode", default=None, metavar="NAME",
+                    help="time decoding on a named decoding workload instead (decode_gqa_bf16)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to scale HBM byte counters")
     args = ap.parse_args()
@@ -157,6 +268,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "repeats": 3}), flush=True)
         return 0
+    if args.decode:
+        return bench_decode(args)
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -152,6 +152,37 @@ int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v
                           int H, int H_kv, int N, int d, float scale, int causal, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decoding: N_q new queries against a cache of N_k keys and values.  The
+ * article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype
+ * Paved the Way for High-Performance WebGPU Flash Attention 2" names
+ * flash-decoding as a next primitive (section "Next Frontiers in WebGPU ML",
+ * "Broader Opset Support") without defining it; the reading taken: the
+ * forward pass's softmax attention with a rectangular score matrix, the
+ * queries being the last N_q positions of the sequence, so with causal != 0
+ * query i keeps keys j <= N_k - N_q + i (no mask for N_q = 1).
+ *
+ *   q, o   [B, H, N_q, d] (dtype); k, v [B, H_kv, N_k, d] (dtype), H_kv
+ *          dividing H, query head h reading key/value head h / (H / H_kv);
+ *   lse    [B, H, N_q] float, natural log, as fa2_forward.
+ * Arithmetic as fa2_forward in bf16 mode.  The cache is split into chunks
+ * walked by separate workgroups; a second kernel merges their normalised
+ * partial outputs with weights exp(LSE_chunk - max) and rounds O once.  The
+ * split depends only on the sizes, so results are the same bits from run to
+ * run.
+ * Supported: dtype FA2_BF16 with d = 128 (else FA2_ERR_UNSUPPORTED, after the
+ * argument checks).  N_k = 0 with N_q > 0, or causal with N_q > N_k:
+ * FA2_ERR_INVALID_ARG.  B, H or N_q = 0: no-op.
+ * workspace: device memory of at least fa2_decode_workspace_size(...) bytes,
+ * 16-byte aligned (the partial results); may be NULL when that size is 0.
+ * Asynchronous on stream, like the other calls.
+ */
+size_t fa2_decode_workspace_size(int B, int H, int H_kv, int N_q, int N_k, int d, int dtype);
+
+int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+               int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

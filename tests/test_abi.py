@@ -33,8 +33,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert names == ["fa2_backward", "fa2_backward_ex", "fa2_backward_stage", "fa2_backward_stage_ex",
-                     "fa2_backward_workspace_size", "fa2_backward_workspace_size_ex", "fa2_forward",
-                     "fa2_forward_ex", "fa2_status_string"]
+                     "fa2_backward_workspace_size", "fa2_backward_workspace_size_ex", "fa2_decode",
+                     "fa2_decode_workspace_size", "fa2_forward", "fa2_forward_ex", "fa2_status_string"]
     for n in names:
         assert hasattr(L, n), n
 
@@ -198,3 +198,47 @@ def test_ex_checks_like_the_plain_calls(L):
     assert fwd_ex(L, 4, 2, d=48) == fa.FA2_ERR_UNSUPPORTED
     assert fwd_ex(L, 0, 0, B=1) == fa.FA2_OK  # empty: a no-op
     assert bwd_ex(L, 4, 1, stage=4) == fa.FA2_ERR_INVALID_ARG
+
+
+# Decoding: validation happens before any HIP call.
+def dec(L, B=1, H=4, H_kv=2, Nq=1, Nk=100, d=128, scale=0.125, causal=0, dtype=1, ptr=A, ws=A, wsb=1 << 30):
+    return L.fa2_decode(ptr, ptr, ptr, ptr, ptr, B, H, H_kv, Nq, Nk, d, scale, causal, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), fa.FA2_ERR_INVALID_ARG), (dict(Nq=-1), fa.FA2_ERR_INVALID_ARG),
+    (dict(Nk=-1), fa.FA2_ERR_INVALID_ARG), (dict(H_kv=3), fa.FA2_ERR_INVALID_ARG),
+    (dict(H_kv=0), fa.FA2_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA2_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA2_ERR_INVALID_ARG), (dict(dtype=5), fa.FA2_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA2_ERR_INVALID_ARG), (dict(Nq=5, Nk=4, causal=1), fa.FA2_ERR_INVALID_ARG),
+    (dict(dtype=0), fa.FA2_ERR_UNSUPPORTED), (dict(d=64), fa.FA2_ERR_UNSUPPORTED),
+    (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(ptr=None), fa.FA2_ERR_INVALID_ARG),
+    (dict(ptr=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(Nk=1 << 24), fa.FA2_ERR_INVALID_ARG),
+])
+def test_decode_rejects(L, kw, status):
+    assert dec(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0, H_kv=0), dict(Nq=0)])
+def test_decode_empty_is_noop(L, kw):
+    assert dec(L, ptr=None, ws=None, wsb=0, **kw) == fa.FA2_OK
+
+
+def test_decode_workspace(L):
+    """Partial results of the split cache: S chunks x (O rows in fp32 and
+    their LSE), S from the sizes; none when the cache is one chunk."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    # 16 x 8 key/value heads, one row block each: 512 / 128 = 4 chunks of 128 blocks
+    rows = 16 * 64 * 1
+    assert L.fa2_decode_workspace_size(16, 64, 8, 1, 16384, 128, 1) == al(4 * rows * 128 * 4) + al(4 * rows * 4)
+    # 4 blocks of keys: a single chunk, no workspace
+    assert L.fa2_decode_workspace_size(1, 8, 1, 4, 100, 128, 1) == 0
+    # 33 blocks, at most 8 chunks of >= 4 blocks: chunks of 5 blocks, 7 of them
+    assert L.fa2_decode_workspace_size(1, 1, 1, 100, 1040, 128, 1) == al(7 * 100 * 128 * 4) + al(7 * 100 * 4)
+    assert L.fa2_decode_workspace_size(1, 4, 2, 1, 100, 64, 1) == 0
+    assert L.fa2_decode_workspace_size(1, 4, 3, 1, 100, 128, 1) == 0
+    need = L.fa2_decode_workspace_size(16, 64, 8, 1, 16384, 128, 1)
+    assert dec(L, B=16, H=64, H_kv=8, Nk=16384, wsb=need - 1) == fa.FA2_ERR_WORKSPACE
+    assert dec(L, B=16, H=64, H_kv=8, Nk=16384, ws=None, wsb=need) == fa.FA2_ERR_WORKSPACE
+    assert dec(L, B=16, H=64, H_kv=8, Nk=16384, ws=MIS, wsb=need) == fa.FA2_ERR_UNSUPPORTED

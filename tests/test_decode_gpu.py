@@ -1,0 +1,121 @@
+"""GPU parity of decoding (N_q new queries against an N_k cache) against the
+fp64 oracle's ``decode``.
+
+Same error measure and limits as the forward and backward parity tests
+(err = max|gpu - oracle| / max|oracle|, 2e-2 for bf16 inputs with fp32
+accumulation); outputs are NaN-filled inside canary guard bands before the
+call.  The cases cover the direct path (one chunk) and the split path (a
+partial result per chunk and the merge kernel), ragged caches, more than 32
+rows per key/value head, causal rows that see no key of a chunk, and the
+full-size decoding workload on sampled heads.
+"""
+import pytest
+import torch
+
+import oracle
+import tiled_attention_fwd_amd as fa
+import workloads
+from tests.test_parity_gpu import Guarded, log, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def gpu_decode(q, k, v, causal, scale):
+    B, H, Nq, d = q.shape
+    o = Guarded(q.shape, q.dtype)
+    lse = Guarded((B, H, Nq), torch.float32)
+    fa.fa2_decode(q, k, v, o.t, lse.t, causal, scale)
+    torch.cuda.synchronize()
+    assert o.guards_intact(), "O: write outside the output tensor"
+    assert lse.guards_intact(), "LSE: write outside the output tensor"
+    return o.t, lse.t
+
+
+def run_decode_case(w, heads=None):
+    """heads: (b, key/value head) pairs to compare (with their query heads);
+    None compares everything."""
+    log("decode case: %s seed=%d" % (w.describe(), w.seed))
+    q, k, v = workloads.make_decode_inputs(w, device="cuda")
+    o, lse = gpu_decode(q, k, v, w.causal, w.scale)
+    o, lse = o.float().cpu(), lse.cpu()
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    G = w.H // w.H_kv
+    sel = [(slice(None), slice(None), slice(None))] if heads is None else \
+        [(slice(b, b + 1), slice(h * G, (h + 1) * G), slice(h, h + 1)) for b, h in heads]
+    eo = el = 0.0
+    for bs, hs, ks in sel:
+        o_r, lse_r = oracle.decode(qc[bs, hs], kc[bs, ks], vc[bs, ks], w.scale, w.causal)
+        eo = max(eo, rel_err(o[bs, hs], o_r))
+        el = max(el, rel_err(lse[bs, hs], lse_r))
+    log("  errors: O=%.3g LSE=%.3g" % (eo, el))
+    assert eo <= TOL and el <= TOL, (w.describe(), eo, el)
+    return o, lse
+
+
+def dw(B, H, H_kv, Nq, Nk, causal, seed):
+    return workloads.DecodeWorkload("decode", B, H, H_kv, Nq, Nk, 128, "bf16", causal, seed)
+
+
+DECODE_CASES = [
+    # split cache (8 chunks of 128 keys), ragged end, grouped heads
+    (2, 8, 2, 1, 1000, False),
+    (2, 8, 2, 4, 1000, True),
+    # one chunk (direct output), ragged
+    (1, 4, 4, 3, 70, True),
+    (1, 2, 1, 1, 1, False),
+    (1, 3, 1, 2, 33, True),
+    # 100 rows (4 row blocks); rows i < 20 see no key of the last chunk
+    (1, 1, 1, 100, 1040, True),
+    # 64 rows per key/value head (groups of 8, 8 queries), split
+    (3, 16, 2, 8, 2049, True),
+    # N_q = N_k: the square causal pass
+    (1, 8, 8, 16, 16, True),
+    # many chunks (32 x 128 keys)
+    (2, 6, 3, 5, 4096, False),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,Nq,Nk,causal", DECODE_CASES)
+def test_decode_parity(B, H, H_kv, Nq, Nk, causal):
+    seed = 4000 + 7 * B + 13 * H + H_kv + 31 * Nq + Nk + (1 if causal else 0)
+    run_decode_case(dw(B, H, H_kv, Nq, Nk, causal, seed))
+
+
+def test_decode_workload_sampled_heads():
+    """The decoding workload at full size (16 sequences, 64 query heads over
+    8 key/value heads, one query against a 16 K cache), as the benchmark
+    runs it, on three key/value heads with their 8 query heads each."""
+    run_decode_case(workloads.DECODE_WORKLOADS["decode_gqa_bf16"], heads=[(0, 0), (7, 3), (15, 7)])
+
+
+def test_decode_square_matches_forward():
+    """N_q = N_k causal decoding is the causal forward pass."""
+    w = dw(1, 4, 4, 300, 300, True, 4101)
+    q, k, v = workloads.make_decode_inputs(w, device="cuda")
+    o, lse = gpu_decode(q, k, v, True, w.scale)
+    of, lf = fa.forward(q, k, v, True, w.scale)
+    torch.cuda.synchronize()
+    assert rel_err(o.float().cpu(), of.float().cpu()) < TOL
+    assert rel_err(lse.cpu(), lf.cpu()) < TOL
+
+
+def test_decode_bitwise_repeatable():
+    w = dw(2, 8, 2, 3, 3000, True, 4102)
+    q, k, v = workloads.make_decode_inputs(w, device="cuda")
+    a = fa.decode(q, k, v, True, w.scale)
+    b = fa.decode(q, k, v, True, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_rejects_on_gpu():
+    q = torch.zeros((1, 2, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 3, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.Fa2Error):  # causal with more queries than keys
+        fa.decode(q, k, k, True)
+    q32 = torch.zeros((1, 2, 1, 128), dtype=torch.float32, device="cuda")
+    k32 = torch.zeros((1, 2, 8, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.Fa2Error):  # float32 decoding is not provided
+        fa.decode(q32, k32, k32, False)

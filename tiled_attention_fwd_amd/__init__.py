@@ -8,9 +8,10 @@ library is not built, importing works but every call raises ``Fa2Error``.
 Functions with the C names (``fa2_forward``, ``fa2_backward``,
 ``fa2_backward_stage``, their ``_ex`` forms with a key/value head count for
 grouped-query attention, ``fa2_backward_workspace_size`` (``_ex``),
-``fa2_status_string``) take caller-allocated tensors like the C ABI;
-``forward`` / ``backward`` allocate the outputs (K and V may have fewer heads
-than Q: H_kv dividing H).
+``fa2_decode``, ``fa2_decode_workspace_size``, ``fa2_status_string``) take
+caller-allocated tensors like the C ABI; ``forward`` / ``backward`` /
+``decode`` allocate the outputs (K and V may have fewer heads than Q: H_kv
+dividing H).
 """
 from __future__ import annotations
 
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.fa2_backward_workspace_size.restype = ctypes.c_size_t
         L.fa2_backward_workspace_size_ex.argtypes = [i, i, i, i, i, i]
         L.fa2_backward_workspace_size_ex.restype = ctypes.c_size_t
+        L.fa2_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        L.fa2_decode.restype = i
+        L.fa2_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
+        L.fa2_decode_workspace_size.restype = ctypes.c_size_t
         L.fa2_status_string.argtypes = [i]
         L.fa2_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -217,6 +222,52 @@ def _backward_call(ex, stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, wo
     if st != FA2_OK:
         name = ("fa2_backward" if stage == 0 else "fa2_backward_stage(%d)" % stage) + ("_ex" if ex else "")
         raise Fa2Error(st, name)
+
+
+def fa2_decode_workspace_size(B: int, H: int, H_kv: int, N_q: int, N_k: int, d: int, dtype) -> int:
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().fa2_decode_workspace_size(B, H, H_kv, N_q, N_k, d, code))
+
+
+def fa2_decode(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue decoding of q [B, H, N_q, d] against the cache k, v
+    [B, H_kv, N_k, d] into caller-allocated ``o`` (q's shape) and ``lse``
+    (float32 [B, H, N_q]); causal places the queries at the cache's last
+    N_q positions."""
+    _check_tensors(q, k, v, o, lse)
+    B, H, Nq, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, H_kv, N_k, d] with q's B and d")
+    H_kv, Nk = k.shape[1], k.shape[2]
+    for t in (k, v, o):
+        if t.dtype != q.dtype:
+            raise ValueError("all tensors must share one dtype")
+    if o.shape != q.shape:
+        raise ValueError("o must have q's shape")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N_q]")
+    code = _dtype_code(q.dtype)
+    need = int(lib().fa2_decode_workspace_size(B, H, H_kv, Nq, Nk, d, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fa2_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, Nq,
+                          Nk, d, _scale(scale, d), int(bool(causal)), code, ws_ptr, ws_bytes,
+                          _stream(stream, q.device))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_decode")
+
+
+def decode(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Return (o, lse) of q [B, H, N_q, d] against the cache k, v
+    [B, H_kv, N_k, d] (bfloat16, d = 128)."""
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa2_decode(q, k, v, o, lse, causal, scale, None, stream)
+    return o, lse
 
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, stream=None):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa2.so")
-SOURCES = ["fa2_api.cpp", "fa2_fwd.hip", "fa2_bwd.hip"]
+SOURCES = ["fa2_api.cpp", "fa2_fwd.hip", "fa2_bwd.hip", "fa2_decode.hip"]
 ARCH = "gfx950"
 
 

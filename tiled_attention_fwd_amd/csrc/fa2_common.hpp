@@ -53,6 +53,10 @@ struct BoolC {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescaling of the online softmax: the running max (base-2 units) only
+// moves when a block's max exceeds it by more than this, so weights stay
+// below 2^kSlack, harmless in fp32 accumulators and bf16 operands.
+constexpr float kSlack = 8.0f;
 
 template <typename T>
 struct Elt;

@@ -40,8 +40,6 @@
 
 namespace fa2 {
 
-constexpr float kSlack = 8.0f;
-
 template <typename T, int D>
 struct FwdTile {
   static constexpr int NW = 4;

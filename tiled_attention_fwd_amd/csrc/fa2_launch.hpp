@@ -75,7 +75,55 @@ inline size_t ws_part_bytes(int B, int Hkv, int N, int d, int S) {
   return S > 1 ? 2 * align256((size_t)S * B * Hkv * N * d * sizeof(float)) : 0;
 }
 
+// Decoding (bf16, d = 128): N_q queries [B, H, N_q, d] against a cache
+// k, v [B, Hkv, N_k, d]; the workspace holds the chunks' partial results.
+struct DecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  float* workspace;
+  hipStream_t stream;
+};
+
+// How the decode pass is cut: row blocks of 32 of the G * N_q rows of a
+// key/value head, and the cache split into chunks of chunk_blocks 32-key
+// blocks.  Splits are added until there are about kDecodeWorkgroups
+// workgroups (one wave each, two per CU: one round over the device; more,
+// shorter chunks measured slower, each chunk paying its own load latency
+// before its ring fills), keeping chunks of at least 4 blocks; no chunk is
+// left empty.
+constexpr long long kDecodeWorkgroups = 512;
+struct DecodePlan {
+  int row_blocks, splits, chunk_blocks;
+};
+inline DecodePlan decode_plan(int B, int H, int Hkv, int Nq, int Nk) {
+  DecodePlan p;
+  const long long M = (long long)(H / Hkv) * Nq;
+  p.row_blocks = (int)((M + 31) / 32);
+  const int nbk = (Nk + 31) / 32;
+  const long long base = (long long)B * Hkv * p.row_blocks;
+  long long want = (kDecodeWorkgroups + base - 1) / base;
+  const long long most = nbk / 4 > 1 ? nbk / 4 : 1;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  p.chunk_blocks = (int)((nbk + want - 1) / want);
+  p.splits = (nbk + p.chunk_blocks - 1) / p.chunk_blocks;
+  return p;
+}
+inline size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  const DecodePlan p = decode_plan(B, H, Hkv, Nq, Nk);
+  if (p.splits <= 1) return 0;
+  const size_t rows = (size_t)B * H * Nq;
+  return align256((size_t)p.splits * rows * d * sizeof(float)) + align256((size_t)p.splits * rows * sizeof(float));
+}
+
 hipError_t launch_forward(const FwdArgs& a);
+hipError_t launch_decode(const DecArgs& a);
 // stage 1: D = rowsum(dO * O); 2: the dK/dV kernel; 3: the dQ kernel.
 hipError_t launch_backward_stage(const BwdArgs& a, int stage);
 

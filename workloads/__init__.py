@@ -20,6 +20,10 @@ so exact), q and k are multiplied by it.  bf16 workloads then round every
 tensor to bfloat16 (round to nearest even).  Grouped-query cases (``H_kv``
 key/value heads below H) draw k and v with shape [B, H_kv, N, d].  The oracle receives the same
 tensors converted to float64, so input rounding is never counted as error.
+
+Decoding workloads (``DecodeWorkload``: N_q new queries against a cache of
+N_k keys) follow the same recipe with q [B, H, N_q, d] and k, v
+[B, H_kv, N_k, d], drawn in the order q, k, v.
 """
 from __future__ import annotations
 
@@ -101,3 +105,54 @@ def custom(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
            qk_mult: float = 1.0, name: str = "custom", H_kv: int = 0) -> Workload:
     """A workload outside the named five (edge-case shapes in the tests)."""
     return Workload(name, B, H, N, d, dtype, causal, seed, qk_mult, H_kv)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    N_q: int
+    N_k: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def describe(self) -> str:
+        return "%s B%d H%d/kv%d Nq%d Nk%d d%d %s %s" % (
+            self.name, self.B, self.H, self.H_kv, self.N_q, self.N_k, self.d, self.dtype,
+            "causal" if self.causal else "non-causal")
+
+
+# One new token per sequence for 16 sequences of a 64-query-head model with 8
+# key/value heads and a 16 K cache (a 1 GiB bf16 cache: far larger than the
+# device's caches, so every pass reads it from HBM).
+DECODE_WORKLOADS = {
+    "decode_gqa_bf16": DecodeWorkload("decode_gqa_bf16", 16, 64, 8, 1, 16384, 128, "bf16", False, 7),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int | None = None, device: str | torch.device = "cpu"):
+    """Return (q, k, v) for decoding workload ``w`` on ``device`` in its dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else int(seed))
+    q = torch.randn((w.B, w.H, w.N_q, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.H_kv, w.N_k, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.H_kv, w.N_k, w.d), generator=g, dtype=torch.float32)
+    out = []
+    for t in (q, k, v):
+        t = t.to(w.torch_dtype).contiguous()
+        if str(device) != "cpu":
+            t = t.to(device)
+        out.append(t)
+    return tuple(out)

@@ -17,11 +17,12 @@ kernel (its counted FLOP per launch over its mean event-timed duration,
 against the bf16 dense MFMA peak) and the oracle's CPU throughput on a
 bounded sample of heads of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 1..6]
+    python bench.py [--steps K] [--warmup W] [--workload 1..7]
     python bench.py --decode decode_gqa_bf16
 
 Workload 6 is the same shape with grouped-query attention (16 query heads
-over 2 key/value heads); its line is not the headline.  ``--decode`` times
+over 2 key/value heads) and workload 7 the same shape in fp16; their lines
+are not the headline.  ``--decode`` times
 decoding instead (one new query per sequence against a 16 K cache, 64 query
 heads over 8 key/value heads): one step is one ``fa2_decode`` call (the
 split-cache kernel and the merge kernel); it is bound by HBM, so its line
@@ -44,7 +45,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # Public MI355X figures (dense, no sparsity), TFLOP/s.
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s and % MFMA peak (bf16 B4 H16 N4096 d128 causal)"
 CSRC = os.path.join(ROOT, "tiled_attention_fwd_amd", "csrc")

@@ -20,7 +20,8 @@
  * Layout and ownership (every call):
  *   - q, k, v, o, dO, dq, dk, dv are DEVICE pointers to contiguous row-major
  *     [B, H, N, d] arrays of the element type `dtype` (FA2_F32: float,
- *     FA2_BF16: bfloat16).  lse is a device float array [B, H, N].
+ *     FA2_BF16: bfloat16, FA2_F16: IEEE binary16).  lse is a device float
+ *     array [B, H, N].
  *   - Every pointer must be 16-byte aligned.  Outputs must not alias inputs
  *     or each other.
  *   - The caller owns every buffer (inputs, outputs, workspace).  The library
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-typedef enum { FA2_F32 = 0, FA2_BF16 = 1 } fa2_dtype;
+typedef enum { FA2_F32 = 0, FA2_BF16 = 1, FA2_F16 = 2 } fa2_dtype;
 
 typedef enum {
   FA2_OK = 0,
@@ -59,9 +60,12 @@ typedef enum {
 /*
  * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float, natural
  * log).  Arithmetic: the two products run on MFMA with fp32 accumulation
- * (bf16 operands for FA2_BF16, fp32 operands for FA2_F32); the softmax
- * state is fp32; in bf16 mode the weights P are rounded to bf16 (nearest
- * even) before the second product and o is rounded to nearest even.
+ * (bf16 operands for FA2_BF16, fp16 for FA2_F16, fp32 for FA2_F32); the
+ * softmax state is fp32; in the 16-bit modes the weights P are rounded to
+ * the element type (nearest even) before the second product and o is
+ * rounded to nearest even (the backward likewise rounds dS).  The article
+ * names half-precision floats as a source of rounding error to watch
+ * (section "Numerical Stability and Loss Drift"); FA2_F16 is that type.
  * scale: the factor on q . k (commonly 1/sqrt(d)); must be finite and > 0.
  * causal: nonzero keeps keys j <= i (top-left aligned).
  */
@@ -165,12 +169,12 @@ int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v
  *   q, o   [B, H, N_q, d] (dtype); k, v [B, H_kv, N_k, d] (dtype), H_kv
  *          dividing H, query head h reading key/value head h / (H / H_kv);
  *   lse    [B, H, N_q] float, natural log, as fa2_forward.
- * Arithmetic as fa2_forward in bf16 mode.  The cache is split into chunks
+ * Arithmetic as fa2_forward in the 16-bit modes.  The cache is split into chunks
  * walked by separate workgroups; a second kernel merges their normalised
  * partial outputs with weights exp(LSE_chunk - max) and rounds O once.  The
  * split depends only on the sizes, so results are the same bits from run to
  * run.
- * Supported: dtype FA2_BF16 with d = 128 (else FA2_ERR_UNSUPPORTED, after the
+ * Supported: dtype FA2_BF16 or FA2_F16 with d = 128 (else FA2_ERR_UNSUPPORTED, after the
  * argument checks).  N_k = 0 with N_q > 0, or causal with N_q > N_k:
  * FA2_ERR_INVALID_ARG.  B, H or N_q = 0: no-op.
  * workspace: device memory of at least fa2_decode_workspace_size(...) bytes,

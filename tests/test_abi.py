@@ -61,7 +61,7 @@ def test_forward_null_pointer(L, arg):
     (dict(B=-1), fa.FA2_ERR_INVALID_ARG), (dict(H=-2), fa.FA2_ERR_INVALID_ARG),
     (dict(N=-3), fa.FA2_ERR_INVALID_ARG), (dict(d=0), fa.FA2_ERR_INVALID_ARG),
     (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(d=256), fa.FA2_ERR_UNSUPPORTED),
-    (dict(dtype=2), fa.FA2_ERR_INVALID_ARG), (dict(dtype=-1), fa.FA2_ERR_INVALID_ARG),
+    (dict(dtype=3), fa.FA2_ERR_INVALID_ARG), (dict(dtype=-1), fa.FA2_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA2_ERR_INVALID_ARG), (dict(scale=-0.5), fa.FA2_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA2_ERR_INVALID_ARG), (dict(scale=float("inf")), fa.FA2_ERR_INVALID_ARG),
     (dict(q=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(lse=MIS), fa.FA2_ERR_UNSUPPORTED),
@@ -100,6 +100,7 @@ def test_workspace_size_formula(L):
     rows = B * H * N
     assert L.fa2_backward_workspace_size(B, H, N, d, 1) == 2 * al(rows * 4)
     assert L.fa2_backward_workspace_size(B, H, N, d, 0) == 2 * al(rows * 4)
+    assert L.fa2_backward_workspace_size(B, H, N, d, 2) == 2 * al(rows * 4)
     assert L.fa2_backward_workspace_size(0, H, N, d, 1) == 0
     assert L.fa2_backward_workspace_size(B, H, N, 40, 1) == 0
     assert L.fa2_backward_workspace_size(-1, H, N, d, 1) == 0
@@ -125,6 +126,7 @@ def test_workspace_size_ex_formula(L):
     # enough workgroups already (16 x 8 x 8 = 1024), fp32, or another head size: no partials
     assert L.fa2_backward_workspace_size_ex(8, 16, 8, 2048, d, 1) == 2 * al(8 * 16 * 2048 * 4)
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 0) == plain
+    assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 2) == plain + 2 * al(4 * B * 2 * N * d * 4)
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, 64, 1) == plain
     assert L.fa2_backward_workspace_size_ex(B, H, 3, N, d, 1) == 0
     assert L.fa2_backward_workspace_size_ex(0, H, 2, N, d, 1) == 0
@@ -212,6 +214,7 @@ def dec(L, B=1, H=4, H_kv=2, Nq=1, Nk=100, d=128, scale=0.125, causal=0, dtype=1
     (dict(scale=float("nan")), fa.FA2_ERR_INVALID_ARG), (dict(dtype=5), fa.FA2_ERR_INVALID_ARG),
     (dict(Nk=0), fa.FA2_ERR_INVALID_ARG), (dict(Nq=5, Nk=4, causal=1), fa.FA2_ERR_INVALID_ARG),
     (dict(dtype=0), fa.FA2_ERR_UNSUPPORTED), (dict(d=64), fa.FA2_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA2_ERR_INVALID_ARG), (dict(d=64, dtype=2), fa.FA2_ERR_UNSUPPORTED),
     (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(ptr=None), fa.FA2_ERR_INVALID_ARG),
     (dict(ptr=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(Nk=1 << 24), fa.FA2_ERR_INVALID_ARG),
 ])
@@ -237,6 +240,8 @@ def test_decode_workspace(L):
     # 33 blocks, at most 8 chunks of >= 4 blocks: chunks of 5 blocks, 7 of them
     assert L.fa2_decode_workspace_size(1, 1, 1, 100, 1040, 128, 1) == al(7 * 100 * 128 * 4) + al(7 * 100 * 4)
     assert L.fa2_decode_workspace_size(1, 4, 2, 1, 100, 64, 1) == 0
+    assert L.fa2_decode_workspace_size(16, 64, 8, 1, 16384, 128, 2) == al(4 * rows * 128 * 4) + al(4 * rows * 4)
+    assert L.fa2_decode_workspace_size(16, 64, 8, 1, 16384, 128, 0) == 0
     assert L.fa2_decode_workspace_size(1, 4, 3, 1, 100, 128, 1) == 0
     need = L.fa2_decode_workspace_size(16, 64, 8, 1, 16384, 128, 1)
     assert dec(L, B=16, H=64, H_kv=8, Nk=16384, wsb=need - 1) == fa.FA2_ERR_WORKSPACE

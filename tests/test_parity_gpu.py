@@ -3,7 +3,10 @@
 Error measure, per tensor T in (O, LSE, dQ, dK, dV):
     err(T) = max |T_gpu - T_oracle| / max |T_oracle|
 with limits 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs with fp32
-accumulation.  The oracle runs on the GPU's exact input values (bf16 inputs
+accumulation.  Half precision has no stated limit; it is derived from the
+bfloat16 one: the errors come from rounding P, dS and the outputs to the
+element type, whose unit roundoff is 2^-11 for fp16 against 2^-8 for bf16,
+so the fp16 limit is 2e-2 * 2^-3 = 2.5e-3.  The oracle runs on the GPU's exact input values (bf16 inputs
 are converted to float64), so input rounding is not counted.  The GPU
 backward consumes the GPU forward's own O and LSE.
 
@@ -25,7 +28,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2.5e-3}
 GUARD = 4096  # elements of guard band on each side of every output
 CANARY = -12288.0  # exactly representable in bf16 and fp32
 
@@ -126,10 +129,22 @@ def test_large_causal_bf16_sampled_heads():
     run_case(w, heads=[(0, 0), (2, 9), (3, 15)])
 
 
+def test_large_causal_f16_sampled_heads():
+    """The large causal shape in IEEE half precision (workload 7)."""
+    run_case(workloads.WORKLOADS[7], heads=[(0, 0), (1, 6), (3, 15)])
+
+
+def test_ragged_noncausal_f16_stress_sampled_heads():
+    """Workload 5's ragged non-causal stress case (q, k x 8: logits of about
+    64 nats, many rescales) in half precision."""
+    w = workloads.custom(16, 12, 1000, 64, "f16", False, 3201, 8.0, name="ragged_noncausal_f16")
+    run_case(w, heads=[(0, 0), (7, 5), (15, 11)])
+
+
 EDGE_N = [1, 2, 17, 63, 64, 65, 127, 129, 1000]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("N", EDGE_N)
@@ -225,7 +240,7 @@ def test_lse_accuracy_bf16_tighter_than_tolerance():
 GQA_CASES = [(8, 2), (6, 1), (4, 4)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("H,H_kv", GQA_CASES)

@@ -23,6 +23,7 @@ import torch
 
 FA2_F32 = 0
 FA2_BF16 = 1
+FA2_F16 = 2
 FA2_OK = 0
 FA2_ERR_INVALID_ARG = 1
 FA2_ERR_UNSUPPORTED = 2
@@ -88,7 +89,9 @@ def _dtype_code(t: torch.dtype) -> int:
         return FA2_F32
     if t == torch.bfloat16:
         return FA2_BF16
-    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t)
+    if t == torch.float16:
+        return FA2_F16
+    raise TypeError("unsupported dtype %s (float32, bfloat16 or float16)" % t)
 
 
 def _check_tensors(ref: torch.Tensor, *ts: torch.Tensor):
@@ -262,7 +265,7 @@ def fa2_decode(q, k, v, o, lse, causal: bool = False, scale: float | None = None
 
 def decode(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
     """Return (o, lse) of q [B, H, N_q, d] against the cache k, v
-    [B, H_kv, N_k, d] (bfloat16, d = 128)."""
+    [B, H_kv, N_k, d] (bfloat16 or float16, d = 128)."""
     B, H, Nq, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)

@@ -19,7 +19,7 @@ bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 // Shared size/type checks.  Returns FA2_OK, or the status to report.
 int check_sizes(int B, int H, int N, int d, int dtype) {
   if (B < 0 || H < 0 || N < 0 || d <= 0) return FA2_ERR_INVALID_ARG;
-  if (dtype != FA2_F32 && dtype != FA2_BF16) return FA2_ERR_INVALID_ARG;
+  if (dtype != FA2_F32 && dtype != FA2_BF16 && dtype != FA2_F16) return FA2_ERR_INVALID_ARG;
   if (!supported_d(d)) return FA2_ERR_UNSUPPORTED;
   // Per-head offsets are computed in int; whole-tensor offsets in size_t.
   if ((int64_t)N * d >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;
@@ -139,7 +139,7 @@ int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, c
 
 size_t fa2_decode_workspace_size(int B, int H, int H_kv, int N_q, int N_k, int d, int dtype) {
   if (B <= 0 || H <= 0 || N_q <= 0 || N_k <= 0 || !valid_hkv(H, H_kv)) return 0;
-  if (dtype != FA2_BF16 || d != 128) return 0;
+  if ((dtype != FA2_BF16 && dtype != FA2_F16) || d != 128) return 0;
   if ((int64_t)N_k * d >= ((int64_t)1 << 31) || (int64_t)B * H * N_q >= ((int64_t)1 << 31)) return 0;
   return fa2::decode_ws_bytes(B, H, H_kv, N_q, N_k, d);
 }
@@ -148,7 +148,7 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                int N_k, int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
                void* stream) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0 || d <= 0) return FA2_ERR_INVALID_ARG;
-  if (dtype != FA2_F32 && dtype != FA2_BF16) return FA2_ERR_INVALID_ARG;
+  if (dtype != FA2_F32 && dtype != FA2_BF16 && dtype != FA2_F16) return FA2_ERR_INVALID_ARG;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
   if ((int64_t)N_k * d >= ((int64_t)1 << 31) || (int64_t)N_q * d >= ((int64_t)1 << 31))
@@ -156,7 +156,7 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   if ((int64_t)B * H * N_q >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;
   if (B == 0 || H == 0 || N_q == 0) return FA2_OK;
   if (N_k == 0 || (causal && N_q > N_k)) return FA2_ERR_INVALID_ARG;
-  if (dtype != FA2_BF16 || d != 128) return FA2_ERR_UNSUPPORTED;
+  if ((dtype != FA2_BF16 && dtype != FA2_F16) || d != 128) return FA2_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA2_ERR_UNSUPPORTED;
@@ -165,8 +165,8 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
     if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
   }
-  fa2::DecArgs a{q,     k,           v,     o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0,
-                 static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+  fa2::DecArgs a{q,     k,           v,     o,     lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0,
+                 dtype, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
   return fa2::launch_decode(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 

@@ -69,6 +69,18 @@ __device__ __forceinline__ float dot_chunk<__bf16>(u32x4 a, u32x4 b) {
   return s;
 }
 
+template <>
+__device__ __forceinline__ float dot_chunk<_Float16>(u32x4 a, u32x4 b) {
+  // v_dot2_f32_f16: fp16 products are exact in fp32.
+  const f16x8 ah = __builtin_bit_cast(f16x8, a), bh = __builtin_bit_cast(f16x8, b);
+  float s = 0.f;
+  s = __builtin_amdgcn_fdot2(__builtin_shufflevector(ah, ah, 0, 1), __builtin_shufflevector(bh, bh, 0, 1), s, false);
+  s = __builtin_amdgcn_fdot2(__builtin_shufflevector(ah, ah, 2, 3), __builtin_shufflevector(bh, bh, 2, 3), s, false);
+  s = __builtin_amdgcn_fdot2(__builtin_shufflevector(ah, ah, 4, 5), __builtin_shufflevector(bh, bh, 4, 5), s, false);
+  s = __builtin_amdgcn_fdot2(__builtin_shufflevector(ah, ah, 6, 7), __builtin_shufflevector(bh, bh, 6, 7), s, false);
+  return s;
+}
+
 // D_i = sum_k dO_ik O_ik.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
@@ -527,19 +539,18 @@ using namespace fa2::tiles;
 }  // namespace d128
 
 // Each wave owns 32 keys; all four walk every 32-row query step.
-template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __restrict__ Q,
-                                                               const __bf16* __restrict__ K,
-                                                               const __bf16* __restrict__ V,
-                                                               const __bf16* __restrict__ dO,
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restrict__ Q,
+                                                               const T* __restrict__ K,
+                                                               const T* __restrict__ V,
+                                                               const T* __restrict__ dO,
                                                                const float* __restrict__ Lse2,
                                                                const float* __restrict__ Delta,
-                                                               __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                                                               T* __restrict__ dK, T* __restrict__ dV,
                                                                int N, int BHkv, float sl2, float scale, int H,
                                                                int G, int S, float* __restrict__ PartK,
                                                                float* __restrict__ PartV) {
   using namespace d128;
-  typedef __bf16 T;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) T Vs[BC * ROWE];         // 32 KB
   __shared__ __attribute__((aligned(16))) T QdO[2][2][TILE_E];     // [buf][Q|dO], 32 KB
@@ -771,17 +782,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const __bf16* __r
 // into a ring of 4 slots (unpadded swizzled rows), issued 3 blocks ahead,
 // one barrier per block; lane offsets of every fragment and load are
 // computed once and the block loop is unrolled over the ring.
-template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const __bf16* __restrict__ Q,
-                                                              const __bf16* __restrict__ K,
-                                                              const __bf16* __restrict__ V,
-                                                              const __bf16* __restrict__ dO,
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict__ Q,
+                                                              const T* __restrict__ K,
+                                                              const T* __restrict__ V,
+                                                              const T* __restrict__ dO,
                                                               const float* __restrict__ Lse2,
                                                               const float* __restrict__ Delta,
-                                                              __bf16* __restrict__ dQ, int N, int BH, int num_qt,
+                                                              T* __restrict__ dQ, int N, int BH, int num_qt,
                                                               float sl2, float scale, int H, int G) {
   using namespace tiles;
-  typedef __bf16 T;
   constexpr int D = 128, KB = 32, BLK_E = KB * 128, CH = 8, DCH = D / 16, NB = D / 32;
   constexpr int QB = 128;           // query rows per workgroup (4 waves x 32)
   constexpr int R = 4, PF = R - 1;  // ring slots, blocks loaded ahead
@@ -973,24 +983,36 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
                        rows);
     return hipGetLastError();
   }
-  if (stage == 2 && sizeof(T) == 2 && D == 128) {
-    const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BHkv;
-    if (blocks * a.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const int S = a.splits;
-    const long long n = (long long)BHkv * a.N * D;  // elements of dK (and of dV)
-    float* part_k = a.part;
-    float* part_v = a.part + align256((size_t)S * n * sizeof(float)) / sizeof(float);
-    hipLaunchKernelGGL((bwd_dkdv_d128_kernel<CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
-                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G,
-                       S, part_k, part_v);
-    if (S > 1) {
-      const unsigned rb = (unsigned)((n / 4 + 255) / 256);
-      hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<__bf16>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,
-                         static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), n, S);
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (stage == 2) {
+      const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BHkv;
+      if (blocks * a.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      const int S = a.splits;
+      const long long n = (long long)BHkv * a.N * D;  // elements of dK (and of dV)
+      float* part_k = a.part;
+      float* part_v = a.part + align256((size_t)S * n * sizeof(float)) / sizeof(float);
+      hipLaunchKernelGGL((bwd_dkdv_d128_kernel<T, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                         static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse2, a.delta,
+                         static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G,
+                         S, part_k, part_v);
+      if (S > 1) {
+        const unsigned rb = (unsigned)((n / 4 + 255) / 256);
+        hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,
+                           static_cast<T*>(a.dk), static_cast<T*>(a.dv), n, S);
+      }
+      return hipGetLastError();
     }
-    return hipGetLastError();
+    if (stage == 3) {
+      const int num_qt = (a.N + 127) / 128;
+      const long long blocks = (long long)num_qt * BH;
+      if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((bwd_dq_d128_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                         static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse2, a.delta,
+                         static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G);
+      return hipGetLastError();
+    }
   }
   if (stage == 2) {
     using C = DkdvTile<T, D>;
@@ -1000,16 +1022,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
                        a.N, BHkv, sl2, a.scale, a.H, G);
-    return hipGetLastError();
-  }
-  if (stage == 3 && sizeof(T) == 2 && D == 128) {
-    const int num_qt = (a.N + 127) / 128;
-    const long long blocks = (long long)num_qt * BH;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_d128_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse2, a.delta,
-                       static_cast<__bf16*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G);
     return hipGetLastError();
   }
   if (stage == 3) {
@@ -1040,6 +1052,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, int stage) {
 hipError_t launch_backward_stage(const BwdArgs& a, int stage) {
   if (a.dtype == kBF16)
     return a.causal ? launch_bwd_d<__bf16, true>(a, stage) : launch_bwd_d<__bf16, false>(a, stage);
+  if (a.dtype == kF16)
+    return a.causal ? launch_bwd_d<_Float16, true>(a, stage) : launch_bwd_d<_Float16, false>(a, stage);
   return a.causal ? launch_bwd_d<float, true>(a, stage) : launch_bwd_d<float, false>(a, stage);
 }
 

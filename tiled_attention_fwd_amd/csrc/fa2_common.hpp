@@ -37,6 +37,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Reinterpret whole 16-byte fragments.  (Bit-casting a single element of an
 // ext_vector, as in __builtin_bit_cast(float, v[e]), is miscompiled by the
@@ -68,6 +70,10 @@ template <>
 struct Elt<__bf16> {
   static constexpr int CH = 8;
 };
+template <>
+struct Elt<_Float16> {
+  static constexpr int CH = 8;
+};
 
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -95,6 +101,12 @@ __device__ __forceinline__ void mfma_chunk<__bf16>(f32x16& acc, u32x4 a, u32x4 b
 }
 
 template <>
+__device__ __forceinline__ void mfma_chunk<_Float16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0,
+                                                0, 0);
+}
+
+template <>
 __device__ __forceinline__ void mfma_chunk<float>(f32x16& acc, u32x4 a, u32x4 b) {
   const f32x4 af = as_f32x4(a), bf = as_f32x4(b);
 #pragma unroll
@@ -102,7 +114,7 @@ __device__ __forceinline__ void mfma_chunk<float>(f32x16& acc, u32x4 a, u32x4 b)
 }
 
 // Pack accumulator registers CH*t .. CH*t+CH-1 into one B-operand fragment
-// (bf16: round to nearest even, two per dword).
+// (bf16, fp16: round to nearest even, two per dword).
 template <typename T>
 __device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int t);
 
@@ -113,6 +125,17 @@ __device__ __forceinline__ u32x4 pack_chunk<__bf16>(const f32x16& x, int t) {
   for (int w = 0; w < 4; ++w) {
     f32x2 pr = {x[8 * t + 2 * w], x[8 * t + 2 * w + 1]};
     r[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+  }
+  return r;
+}
+
+template <>
+__device__ __forceinline__ u32x4 pack_chunk<_Float16>(const f32x16& x, int t) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f32x2 pr = {x[8 * t + 2 * w], x[8 * t + 2 * w + 1]};
+    r[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));
   }
   return r;
 }
@@ -139,6 +162,17 @@ __device__ __forceinline__ float add_fragment_sum<__bf16>(float acc, u32x4 v) {
 }
 
 template <>
+__device__ __forceinline__ float add_fragment_sum<_Float16>(float acc, u32x4 v) {
+  const f16x8 b = __builtin_bit_cast(f16x8, v);
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 6, 7), one, acc, false);
+  return acc;
+}
+
+template <>
 __device__ __forceinline__ float add_fragment_sum<float>(float acc, u32x4 v) {
   const f32x4 f = as_f32x4(v);
   return acc + ((f[0] + f[1]) + (f[2] + f[3]));
@@ -158,6 +192,13 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, float a, float b, fl
   f32x2 lo = {a, b}, hi = {c, d};
   *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
                                          __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+}
+
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* dst, float a, float b, float c, float d) {
+  f32x2 lo = {a, b}, hi = {c, d};
+  *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2)),
+                                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2))};
 }
 
 // A single element converted from fp32.
@@ -196,6 +237,13 @@ __device__ __forceinline__ void write_transposed4<__bf16>(__bf16* tile, int row_
     *reinterpret_cast<u32x2*>(tile + (col0 + 2 * w) * row_stride + pos) = u32x2{lo0, hi0};
     *reinterpret_cast<u32x2*>(tile + (col0 + 2 * w + 1) * row_stride + pos) = u32x2{lo1, hi1};
   }
+}
+
+// fp16 moves the same 16-bit patterns as bf16.
+template <>
+__device__ __forceinline__ void write_transposed4<_Float16>(_Float16* tile, int row_stride, int col0, int pos,
+                                                            const u32x4 (&r)[4]) {
+  write_transposed4<__bf16>(reinterpret_cast<__bf16*>(tile), row_stride, col0, pos, r);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -285,6 +333,12 @@ __device__ __forceinline__ u32x4 load_rowcontract<__bf16>(const __bf16* tile, in
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(u32x4, both);
+}
+
+template <>
+__device__ __forceinline__ u32x4 load_rowcontract<_Float16>(const _Float16* tile, int stride, int rb, int t, int cb,
+                                                            int cmask, int lane) {
+  return load_rowcontract<__bf16>(reinterpret_cast<const __bf16*>(tile), stride, rb, t, cb, cmask, lane);
 }
 
 template <>

@@ -1,5 +1,5 @@
 // fa2_decode.hip -- flash-decoding: a few new queries against a long key/value
-// cache, bf16, d = 128.
+// cache, bf16 or fp16, d = 128.
 //
 // The article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype
 // Paved the Way for High-Performance WebGPU Flash Attention 2" names
@@ -60,15 +60,14 @@ __device__ __forceinline__ void wait_blocks() {
 // and LSE; otherwise its normalised O rows (fp32) and base-2 LSE go to
 // PartO[sp], PartL[sp] (LSE = -inf and O = 0 for a row that sees no key of
 // the chunk).
-template <bool CAUSAL>
-__global__ __launch_bounds__(64) void decode_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                                                    const __bf16* __restrict__ V, __bf16* __restrict__ O,
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                    const T* __restrict__ V, T* __restrict__ O,
                                                     float* __restrict__ LSE, float* __restrict__ PartO,
                                                     float* __restrict__ PartL, int Nq, int Nk, int H, int G,
                                                     int Hkv, int n_rb, int S, int cb, long long rows,
                                                     float sl2) {
   using namespace tiles;
-  typedef __bf16 T;
   constexpr int D = dec::D, KB = dec::KB, BLK_E = dec::BLK_E, R = dec::R, PF = dec::PF;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) T Ks[R][BLK_E];
@@ -273,10 +272,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const __bf16* __restrict__ Q
 // L* = max_s L_s, w_s = 2^(L_s - L*), O = sum_s w_s O_s / sum_s w_s and
 // LSE = (L* + log2 sum_s w_s) ln 2.  32 threads per row, 4 elements each;
 // every row has at least one chunk with a visible key, so L* is finite.
+template <typename T>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ PartO,
-                                                           const float* __restrict__ PartL,
-                                                           __bf16* __restrict__ O, float* __restrict__ LSE,
-                                                           long long rows, int S) {
+                                                           const float* __restrict__ PartL, T* __restrict__ O,
+                                                           float* __restrict__ LSE, long long rows, int S) {
   constexpr int D = dec::D;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = idx / (D / 4);
@@ -292,13 +291,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     acc += w * *reinterpret_cast<const f32x4*>(PartO + ((size_t)s * rows + row) * D + c);
   }
   const float inv = 1.0f / wsum;
-  store4<__bf16>(O + row * D + c, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  store4<T>(O + row * D + c, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   if (c == 0) LSE[row] = (mx + log2f(wsum)) * kLn2;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecArgs& a) {
+template <typename T>
+static hipError_t launch_decode_t(const DecArgs& a) {
   const DecodePlan p = decode_plan(a.B, a.H, a.Hkv, a.Nq, a.Nk);
   const long long rows = (long long)a.B * a.H * a.Nq;
   const long long blocks = (long long)a.B * a.Hkv * p.splits * p.row_blocks;
@@ -308,21 +308,25 @@ hipError_t launch_decode(const DecArgs& a) {
   const float sl2 = a.scale * kLog2e;
   const int G = a.H / a.Hkv;
   if (a.causal)
-    hipLaunchKernelGGL((decode_kernel<true>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, part_o, part_l, a.Nq,
-                       a.Nk, a.H, G, a.Hkv, p.row_blocks, p.splits, p.chunk_blocks, rows, sl2);
+    hipLaunchKernelGGL((decode_kernel<T, true>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<T*>(a.o), a.lse, part_o, part_l, a.Nq, a.Nk, a.H, G, a.Hkv, p.row_blocks,
+                       p.splits, p.chunk_blocks, rows, sl2);
   else
-    hipLaunchKernelGGL((decode_kernel<false>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, part_o, part_l, a.Nq,
-                       a.Nk, a.H, G, a.Hkv, p.row_blocks, p.splits, p.chunk_blocks, rows, sl2);
+    hipLaunchKernelGGL((decode_kernel<T, false>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<T*>(a.o), a.lse, part_o, part_l, a.Nq, a.Nk, a.H, G, a.Hkv, p.row_blocks,
+                       p.splits, p.chunk_blocks, rows, sl2);
   if (p.splits > 1) {
     const long long threads = rows * (dec::D / 4);
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, a.stream,
-                       part_o, part_l, static_cast<__bf16*>(a.o), a.lse, rows, p.splits);
+    hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, a.stream,
+                       part_o, part_l, static_cast<T*>(a.o), a.lse, rows, p.splits);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecArgs& a) {
+  return a.dtype == kF16 ? launch_decode_t<_Float16>(a) : launch_decode_t<__bf16>(a);
 }
 
 }  // namespace fa2

@@ -254,13 +254,12 @@ constexpr int KB = 32;         // keys per block
 constexpr int BLK_E = KB * ROWE;
 }  // namespace fpp
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                        const T* __restrict__ V, T* __restrict__ O,
                                                         float* __restrict__ LSE, int N, int BH, int num_qt,
                                                         float sl2, int H, int G) {
   using namespace tiles;
-  typedef __bf16 T;
   constexpr int D = fpp::D, KB = fpp::KB, BLK_E = fpp::BLK_E;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
   constexpr int R = 4, PF = R - 1;  // ring slots, blocks loaded ahead
@@ -449,15 +448,14 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const __bf16* __restrict
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  if (sizeof(T) == 2 && D == 128) {
+  if constexpr (sizeof(T) == 2 && D == 128) {
     const int BH = a.B * a.H;
     const int num_qt = (a.N + fpp::BR - 1) / fpp::BR;
     const long long blocks = (long long)num_qt * BH;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, BH, num_qt,
-                       a.scale * kLog2e, a.H, a.H / a.Hkv);
+    hipLaunchKernelGGL((fwd_pp_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, a.scale * kLog2e, a.H, a.H / a.Hkv);
     return hipGetLastError();
   }
   using C = FwdTile<T, D>;
@@ -486,6 +484,8 @@ static hipError_t launch_fwd_d(const FwdArgs& a) {
 hipError_t launch_forward(const FwdArgs& a) {
   if (a.dtype == kBF16)
     return a.causal ? launch_fwd_d<__bf16, true>(a) : launch_fwd_d<__bf16, false>(a);
+  if (a.dtype == kF16)
+    return a.causal ? launch_fwd_d<_Float16, true>(a) : launch_fwd_d<_Float16, false>(a);
   return a.causal ? launch_fwd_d<float, true>(a) : launch_fwd_d<float, false>(a);
 }
 

@@ -11,6 +11,7 @@ namespace fa2 {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
+constexpr int kF16 = 2;
 
 struct FwdArgs {
   const void* q;
@@ -56,13 +57,13 @@ inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return 2 *
 
 // How many workgroups share one key/value head's group of G query heads in
 // the dK/dV stage.  One workgroup per (key/value head, 128-key tile) walks
-// the whole group, which leaves few workgroups when G is large; the bf16,
+// the whole group, which leaves few workgroups when G is large; the 16-bit,
 // d = 128 kernel then splits the group over S workgroups (S divides G) until
 // there are at least 1024 of them (four per CU: with causal masking the key
 // tiles differ in cost, and two per CU left the heavy ones as a tail), and a
 // second kernel sums the S partial results in a fixed order.
 inline int dkdv_splits(int B, int Hkv, int G, int N, int d, int dtype) {
-  if (G <= 1 || d != 128 || dtype != kBF16) return 1;
+  if (G <= 1 || d != 128 || dtype == kF32) return 1;
   const long long base = (long long)((N + 127) / 128) * B * Hkv;
   int S = 1;
   while (S < G && base * S < 1024) {
@@ -75,7 +76,7 @@ inline size_t ws_part_bytes(int B, int Hkv, int N, int d, int S) {
   return S > 1 ? 2 * align256((size_t)S * B * Hkv * N * d * sizeof(float)) : 0;
 }
 
-// Decoding (bf16, d = 128): N_q queries [B, H, N_q, d] against a cache
+// Decoding (bf16 or fp16, d = 128): N_q queries [B, H, N_q, d] against a cache
 // k, v [B, Hkv, N_k, d]; the workspace holds the chunks' partial results.
 struct DecArgs {
   const void* q;
@@ -86,6 +87,7 @@ struct DecArgs {
   int B, H, Hkv, Nq, Nk, d;
   float scale;
   bool causal;
+  int dtype;
   float* workspace;
   hipStream_t stream;
 };

@@ -17,7 +17,8 @@ Recipe (identical for every workload): a CPU ``torch.Generator`` seeded with
 the workload's seed draws ``torch.randn`` tensors of shape [B, H, N, d] in
 float32, in the order q, k, v, dO.  Where ``qk_mult`` is not 1 (a power of two,
 so exact), q and k are multiplied by it.  bf16 workloads then round every
-tensor to bfloat16 (round to nearest even).  Grouped-query cases (``H_kv``
+tensor to bfloat16 (round to nearest even), f16 workloads to IEEE half
+precision (round to nearest even).  Grouped-query cases (``H_kv``
 key/value heads below H) draw k and v with shape [B, H_kv, N, d].  The oracle receives the same
 tensors converted to float64, so input rounding is never counted as error.
 
@@ -33,6 +34,9 @@ import math
 import torch
 
 
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
@@ -40,7 +44,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     causal: bool
     seed: int
     qk_mult: float = 1.0
@@ -56,7 +60,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return TORCH_DTYPES[self.dtype]
 
     def shape(self):
         return (self.B, self.H, self.N, self.d)
@@ -76,6 +80,8 @@ WORKLOADS = {
     # Grouped-query variant of workload 4: 16 query heads over 2 key/value
     # heads (groups of 8).
     6: Workload("large_causal_gqa_bf16", 4, 16, 4096, 128, "bf16", True, 6, 1.0, 2),
+    # Workload 4 in IEEE half precision.
+    7: Workload("large_causal_f16", 4, 16, 4096, 128, "f16", True, 7),
 }
 
 
@@ -126,7 +132,7 @@ class DecodeWorkload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return TORCH_DTYPES[self.dtype]
 
     def describe(self) -> str:
         return "%s B%d H%d/kv%d Nq%d Nk%d d%d %s %s" % (

@@ -157,6 +157,44 @@ int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Packed ragged batches (variable-length sequences).  The article's forward
+ * pass runs one workgroup per batch entry, head and query tile (section
+ * "Translating to WGSL and Optimizing Passes"); these calls let each batch
+ * entry have its own length.  The reading taken (the pages say nothing about
+ * ragged batches): B sequences packed one after the other along the token
+ * axis of each head,
+ *   q, o, dO, dq  [H, T, d];  k, v, dk, dv  [H_kv, T, d];  lse  [H, T],
+ * sequence b occupying rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head;
+ * attention (and causal masking, top-left) stays inside each sequence.
+ *   cu_seqlens  DEVICE int32 [B + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[B] <= T,
+ *               4-byte aligned.  The library does not read it on the host;
+ *               offsets outside [0, T] are clamped and lengths cut to
+ *               max_seqlen, so inconsistent offsets give wrong results but no
+ *               access outside the tensors.  Rows not covered by any sequence
+ *               are neither read for results nor written.
+ *   max_seqlen  the longest sequence, 0 <= max_seqlen <= T (sizes the grid).
+ * Other arguments, arithmetic and errors as the fixed-length calls (H_kv as
+ * in fa2_forward_ex).  Sequences of length 0 are allowed.
+ */
+int fa2_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int* cu_seqlens, int B, int H, int H_kv, int T, int max_seqlen, int d,
+                       float scale, int causal, int dtype, void* stream);
+
+size_t fa2_backward_workspace_size_varlen(int B, int H, int H_kv, int T, int max_seqlen, int d,
+                                          int dtype);
+
+int fa2_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int B,
+                        int H, int H_kv, int T, int max_seqlen, int d, float scale, int causal,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int B, int H, int H_kv, int T, int max_seqlen,
+                              int d, float scale, int causal, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Decoding: N_q new queries against a cache of N_k keys and values.  The
  * article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype
  * Paved the Way for High-Performance WebGPU Flash Attention 2" names

@@ -33,8 +33,10 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert names == ["fa2_backward", "fa2_backward_ex", "fa2_backward_stage", "fa2_backward_stage_ex",
-                     "fa2_backward_workspace_size", "fa2_backward_workspace_size_ex", "fa2_decode",
-                     "fa2_decode_workspace_size", "fa2_forward", "fa2_forward_ex", "fa2_status_string"]
+                     "fa2_backward_stage_varlen", "fa2_backward_varlen", "fa2_backward_workspace_size",
+                     "fa2_backward_workspace_size_ex", "fa2_backward_workspace_size_varlen", "fa2_decode",
+                     "fa2_decode_workspace_size", "fa2_forward", "fa2_forward_ex", "fa2_forward_varlen",
+                     "fa2_status_string"]
     for n in names:
         assert hasattr(L, n), n
 
@@ -247,3 +249,42 @@ def test_decode_workspace(L):
     assert dec(L, B=16, H=64, H_kv=8, Nk=16384, wsb=need - 1) == fa.FA2_ERR_WORKSPACE
     assert dec(L, B=16, H=64, H_kv=8, Nk=16384, ws=None, wsb=need) == fa.FA2_ERR_WORKSPACE
     assert dec(L, B=16, H=64, H_kv=8, Nk=16384, ws=MIS, wsb=need) == fa.FA2_ERR_UNSUPPORTED
+
+
+# Packed ragged batches: host-side validation (the offsets themselves live on
+# the device and are never read here).
+def fwd_vl(L, cu=A, B=2, H=4, H_kv=2, T=100, mx=60, d=64, dtype=1, ptr=A):
+    return L.fa2_forward_varlen(ptr, ptr, ptr, ptr, ptr, cu, B, H, H_kv, T, mx, d, 0.125, 1, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), fa.FA2_ERR_INVALID_ARG), (dict(T=-1), fa.FA2_ERR_INVALID_ARG),
+    (dict(mx=-1), fa.FA2_ERR_INVALID_ARG), (dict(mx=101), fa.FA2_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA2_ERR_INVALID_ARG), (dict(d=48), fa.FA2_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA2_ERR_INVALID_ARG), (dict(ptr=None), fa.FA2_ERR_INVALID_ARG),
+    (dict(ptr=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(cu=A + 2), fa.FA2_ERR_UNSUPPORTED),
+    (dict(T=1 << 24, mx=10, d=128), fa.FA2_ERR_INVALID_ARG),
+])
+def test_varlen_rejects(L, kw, status):
+    assert fwd_vl(L, **kw) == status
+
+
+def test_varlen_empty_is_noop(L):
+    assert fwd_vl(L, ptr=None, cu=None, B=0) == fa.FA2_OK
+    assert fwd_vl(L, ptr=None, mx=0) == fa.FA2_OK
+    assert fwd_vl(L, ptr=None, H=0, H_kv=0) == fa.FA2_OK
+
+
+def test_varlen_workspace(L):
+    def al(x):
+        return (x + 255) // 256 * 256
+    # rows = H * T for D and LSE * log2(e)
+    assert L.fa2_backward_workspace_size_varlen(3, 4, 4, 1000, 600, 64, 1) == 2 * al(4 * 1000 * 4)
+    # grouped bf16 d=128: 5 key tiles x 3 x 2 = 30 workgroups -> split S = G = 2, partials [2][H_kv * T, d]
+    assert L.fa2_backward_workspace_size_varlen(3, 4, 2, 1000, 600, 128, 1) == \
+        2 * al(4 * 1000 * 4) + 2 * al(2 * 2 * 1000 * 128 * 4)
+    assert L.fa2_backward_workspace_size_varlen(3, 4, 2, 1000, 1001, 128, 1) == 0
+    need = L.fa2_backward_workspace_size_varlen(3, 4, 2, 1000, 600, 128, 1)
+    args = (A,) * 10 + (3, 4, 2, 1000, 600, 128, 0.125, 1, 1, A)
+    assert L.fa2_backward_varlen(*args, need - 1, None) == fa.FA2_ERR_WORKSPACE
+    assert L.fa2_backward_stage_varlen(4, *args, need, None) == fa.FA2_ERR_INVALID_ARG

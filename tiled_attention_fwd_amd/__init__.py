@@ -8,6 +8,7 @@ library is not built, importing works but every call raises ``Fa2Error``.
 Functions with the C names (``fa2_forward``, ``fa2_backward``,
 ``fa2_backward_stage``, their ``_ex`` forms with a key/value head count for
 grouped-query attention, ``fa2_backward_workspace_size`` (``_ex``),
+``fa2_forward_varlen``, ``fa2_backward_varlen`` (packed ragged batches),
 ``fa2_decode``, ``fa2_decode_workspace_size``, ``fa2_status_string``) take
 caller-allocated tensors like the C ABI; ``forward`` / ``backward`` /
 ``decode`` allocate the outputs (K and V may have fewer heads than Q: H_kv
@@ -67,6 +68,14 @@ def lib() -> ctypes.CDLL:
         L.fa2_backward_workspace_size.restype = ctypes.c_size_t
         L.fa2_backward_workspace_size_ex.argtypes = [i, i, i, i, i, i]
         L.fa2_backward_workspace_size_ex.restype = ctypes.c_size_t
+        L.fa2_forward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.fa2_forward_varlen.restype = i
+        L.fa2_backward_varlen.argtypes = [vp] * 10 + [i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        L.fa2_backward_varlen.restype = i
+        L.fa2_backward_stage_varlen.argtypes = [i] + L.fa2_backward_varlen.argtypes
+        L.fa2_backward_stage_varlen.restype = i
+        L.fa2_backward_workspace_size_varlen.argtypes = [i, i, i, i, i, i, i]
+        L.fa2_backward_workspace_size_varlen.restype = ctypes.c_size_t
         L.fa2_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
         L.fa2_decode.restype = i
         L.fa2_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -225,6 +234,85 @@ def _backward_call(ex, stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, wo
     if st != FA2_OK:
         name = ("fa2_backward" if stage == 0 else "fa2_backward_stage(%d)" % stage) + ("_ex" if ex else "")
         raise Fa2Error(st, name)
+
+
+def _varlen_shapes(q, k, v, cu_seqlens, max_seqlen, *qlike):
+    """(B, H, H_kv, T, d) of a packed ragged batch after checking shapes."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed tensors are [H, T, d]")
+    H, T, d = q.shape
+    H_kv = k.shape[0]
+    if k.shape != (H_kv, T, d) or v.shape != k.shape or H_kv == 0 and H != 0 or H_kv and H % H_kv:
+        raise ValueError("k, v must be [H_kv, T, d] with H_kv dividing H = %d" % H)
+    for t in (k, v) + tuple(qlike):
+        if t.dtype != q.dtype:
+            raise ValueError("all tensors must share one dtype")
+    for t in qlike:
+        if t.shape != q.shape:
+            raise ValueError("o, dO, dq must have q's shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda \
+            or not cu_seqlens.is_contiguous() or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be a contiguous int32 GPU tensor [B + 1]")
+    return cu_seqlens.numel() - 1, H, H_kv, T, d
+
+
+def fa2_forward_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, causal: bool = True,
+                       scale: float | None = None, stream=None) -> None:
+    """Forward pass of a packed ragged batch: q, o [H, T, d]; k, v
+    [H_kv, T, d]; lse float32 [H, T]; sequence b is rows cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 of every head."""
+    _check_tensors_any(q, k, v, o, lse)
+    B, H, H_kv, T, d = _varlen_shapes(q, k, v, cu_seqlens, max_seqlen, o)
+    if lse.shape != (H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [H, T]")
+    st = lib().fa2_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  cu_seqlens.data_ptr(), B, H, H_kv, T, int(max_seqlen), d, _scale(scale, d),
+                                  int(bool(causal)), _dtype_code(q.dtype), _stream(stream, q.device))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_forward_varlen")
+
+
+def fa2_backward_workspace_size_varlen(B: int, H: int, H_kv: int, T: int, max_seqlen: int, d: int, dtype) -> int:
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().fa2_backward_workspace_size_varlen(B, H, H_kv, T, max_seqlen, d, code))
+
+
+def fa2_backward_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, max_seqlen: int, causal: bool = True,
+                        scale: float | None = None, workspace: torch.Tensor | None = None, stream=None,
+                        stage: int = 0) -> None:
+    """Backward pass of a packed ragged batch (stage 0: all three kernels,
+    else ``fa2_backward_stage_varlen``); dk, dv have k's shape."""
+    _check_tensors_any(q, k, v, o, dO, lse, dq, dk, dv)
+    B, H, H_kv, T, d = _varlen_shapes(q, k, v, cu_seqlens, max_seqlen, o, dO, dq)
+    if dk.shape != k.shape or dv.shape != k.shape or dk.dtype != q.dtype or dv.dtype != q.dtype:
+        raise ValueError("dk, dv must have k's shape and q's dtype")
+    if lse.shape != (H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [H, T]")
+    need = fa2_backward_workspace_size_varlen(B, H, H_kv, T, int(max_seqlen), d, q.dtype)
+    if workspace is None:
+        if stage:
+            raise ValueError("the stages share state through the workspace: pass one")
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(), B, H, H_kv, T, int(max_seqlen), d,
+            _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    if stage:
+        st = lib().fa2_backward_stage_varlen(int(stage), *args)
+    else:
+        st = lib().fa2_backward_varlen(*args)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_backward_varlen" if not stage else "fa2_backward_stage_varlen(%d)" % stage)
+
+
+def _check_tensors_any(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.device != ts[0].device:
+            raise ValueError("tensors must be on one device")
 
 
 def fa2_decode_workspace_size(B: int, H: int, H_kv: int, N_q: int, N_k: int, d: int, dtype) -> int:

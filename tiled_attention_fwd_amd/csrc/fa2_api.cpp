@@ -47,8 +47,23 @@ const char* fa2_status_string(int status) {
   }
 }
 
-int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
-                   int N, int d, float scale, int causal, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Packed ragged batches: T rows per head, sequences of at most max_seqlen
+// rows (the grid's length), device offsets cu[0..B].
+int check_varlen(const int* cu, int B, int T, int max_seqlen, int d) {
+  if (T < 0 || max_seqlen < 0 || max_seqlen > T) return FA2_ERR_INVALID_ARG;
+  if ((int64_t)T * d >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;
+  if (B > 0 && !cu) return FA2_ERR_INVALID_ARG;
+  if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u)) return FA2_ERR_UNSUPPORTED;
+  return FA2_OK;
+}
+
+// N is the sequence length (fixed) or the longest sequence (cu != null).
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                 int d, float scale, int causal, int dtype, const int* cu, int T, void* stream) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
@@ -57,8 +72,26 @@ int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* 
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA2_ERR_UNSUPPORTED;
-  fa2::FwdArgs a{q, k, v, o, lse, B, H, N, d, H_kv, scale, causal != 0, dtype, static_cast<hipStream_t>(stream)};
+  fa2::FwdArgs a{q,     k,           v,     o, lse, B, H, N, d, H_kv, scale, causal != 0, dtype,
+                 static_cast<hipStream_t>(stream), cu, T};
   return fa2::launch_forward(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                   int N, int d, float scale, int causal, int dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, dtype, nullptr, 0, stream);
+}
+
+int fa2_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                       int B, int H, int H_kv, int T, int max_seqlen, int d, float scale, int causal, int dtype,
+                       void* stream) {
+  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
+  if (st != FA2_OK) return st;
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, max_seqlen, d, scale, causal, dtype, cu_seqlens, T, stream);
 }
 
 int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
@@ -66,11 +99,32 @@ int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse
   return fa2_forward_ex(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of a backward whose query side has `rows` rows and key side
+// `kv_rows` ([B, H, N] and [B, H_kv, N], or [H, T] and [H_kv, T]).
+size_t ws_bytes(int B, int H, int H_kv, int N, int d, int dtype, long long rows, long long kv_rows) {
+  const int S = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
+  return fa2::ws_total_bytes((size_t)rows, d, dtype) + fa2::ws_part_bytes(kv_rows, d, S);
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t fa2_backward_workspace_size_ex(int B, int H, int H_kv, int N, int d, int dtype) {
   if (check_sizes(B, H, N, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
   if (is_empty(B, H, N)) return 0;
-  const int S = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
-  return fa2::ws_total_bytes((size_t)B * H * N, d, dtype) + fa2::ws_part_bytes(B, H_kv, N, d, S);
+  return ws_bytes(B, H, H_kv, N, d, dtype, (long long)B * H * N, (long long)B * H_kv * N);
+}
+
+size_t fa2_backward_workspace_size_varlen(int B, int H, int H_kv, int T, int max_seqlen, int d, int dtype) {
+  if (check_sizes(B, H, max_seqlen, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
+  if (T < 0 || max_seqlen > T || (int64_t)T * d >= ((int64_t)1 << 31)) return 0;
+  if (is_empty(B, H, max_seqlen)) return 0;
+  return ws_bytes(B, H, H_kv, max_seqlen, d, dtype, (long long)H * T, (long long)H_kv * T);
 }
 
 size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
@@ -80,7 +134,7 @@ size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
 static int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v,
                          const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
                          int H, int H_kv, int N, int d, float scale, int causal, int dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, const int* cu = nullptr, int T = 0) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
@@ -90,8 +144,9 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA2_ERR_UNSUPPORTED;
-  const size_t rows = (size_t)B * H * N;
-  if (!workspace || workspace_bytes < fa2_backward_workspace_size_ex(B, H, H_kv, N, d, dtype))
+  const size_t rows = cu ? (size_t)H * T : (size_t)B * H * N;
+  const long long kv_rows = cu ? (long long)H_kv * T : (long long)B * H_kv * N;
+  if (!workspace || workspace_bytes < ws_bytes(B, H, H_kv, N, d, dtype, (long long)rows, kv_rows))
     return FA2_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA2_ERR_UNSUPPORTED;
   float* delta = static_cast<float*>(workspace);
@@ -101,7 +156,7 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   const int splits = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
   fa2::BwdArgs a{q,  k, v, o,     dO,          lse,   dq,    dk,   dv,     B,     H,
                  N,  d, H_kv, scale, causal != 0, dtype, delta, lse2, part, splits,
-                 static_cast<hipStream_t>(stream)};
+                 static_cast<hipStream_t>(stream), cu, T};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
@@ -168,6 +223,28 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   fa2::DecArgs a{q,     k,           v,     o,     lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0,
                  dtype, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
   return fa2::launch_decode(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+int fa2_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int B, int H,
+                        int H_kv, int T, int max_seqlen, int d, float scale, int causal, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
+  if (st != FA2_OK) return st;
+  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal, dtype,
+                       workspace, workspace_bytes, stream, cu_seqlens, T);
+}
+
+int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int B, int H, int H_kv, int T, int max_seqlen, int d,
+                              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
+  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
+  if (st != FA2_OK) return st;
+  return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal,
+                       dtype, workspace, workspace_bytes, stream, cu_seqlens, T);
 }
 
 }  // extern "C"

@@ -131,8 +131,8 @@ struct DkdvTile {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int N,
-    int BHkv, float sl2, float scale, int H, int G) {
+    const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int Nmax,
+    int BHkv, float sl2, float scale, int H, int G, const int* __restrict__ cu, int Ttot) {
   using C = DkdvTile<T, D>;
   constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB, QS = C::QS;
   // Double-buffered query-side tiles: one barrier per query tile.
@@ -146,15 +146,18 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
   const int kt = lin / BHkv;  // ascending: for causal the heaviest key tiles go first
-  const int bhk = lin % BHkv;  // key/value head; it serves query heads bh0 .. bh0 + G - 1
-  const int bh0 = (bhk / (H / G)) * H + (bhk % (H / G)) * G;
-  const size_t base = (size_t)bhk * N * D;
+  const int bhk = lin % BHkv;  // (sequence, key/value head); it serves query heads hk*G .. hk*G + G - 1
+  const int bq = bhk / (H / G), hk = bhk % (H / G);
+  const SeqRows skv = seq_rows(cu, Nmax, Ttot, bq, hk, H / G);
+  const int N = skv.n;  // this sequence's length
+  const size_t base = (size_t)skv.row0 * D;
   // Query-side pointers of the query head being walked (set per head below).
   const T* Qh = Q;
   const T* dOh = dO;
   const float* lseh = LSE;
   const float* dlh = Delta;
   const int kv0 = kt * BC;
+  if (kv0 >= N) return;  // a tile past a shorter packed sequence
   const int kw = kv0 + 32 * w;  // first key of this wave
   const int kj = kw + l32;      // key (accumulator column) owned by this lane
 
@@ -318,11 +321,11 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   // attention), accumulating into the same dK, dV.
   const int qt_mask_end = (kv0 + BC > N) ? n_qt : (CAUSAL ? min(n_qt, (kv0 + BC - 1) / BR + 1) : qt_begin);
   for (int g = 0; g < G; ++g) {
-    const int bh = bh0 + g;
-    Qh = Q + (size_t)bh * N * D;
-    dOh = dO + (size_t)bh * N * D;
-    lseh = LSE + (size_t)bh * N;
-    dlh = Delta + (size_t)bh * N;
+    const long long qrow0 = seq_rows(cu, Nmax, Ttot, bq, hk * G + g, H).row0;
+    Qh = Q + (size_t)qrow0 * D;
+    dOh = dO + (size_t)qrow0 * D;
+    lseh = LSE + qrow0;
+    dlh = Delta + qrow0;
     if (qt_begin < n_qt) {
       load_q(qt_begin);
       store_q(0);
@@ -381,8 +384,9 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ dO,
                                                         const float* __restrict__ LSE,
-                                                        const float* __restrict__ Delta, T* __restrict__ dQ, int N,
-                                                        int BH, int num_qt, float sl2, float scale, int H, int G) {
+                                                        const float* __restrict__ Delta, T* __restrict__ dQ, int Nmax,
+                                                        int BH, int num_qt, float sl2, float scale, int H, int G,
+                                                        const int* __restrict__ cu, int Ttot) {
   using C = DqTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -394,11 +398,14 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   const int lin = blockIdx.x;
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
-  const size_t base = (size_t)bh * N * D;
-  const size_t kv_base = (size_t)kv_head(bh, H, G) * N * D;
+  const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
+  const int N = sq.n;  // this sequence's length
+  const size_t base = (size_t)sq.row0 * D;
+  const size_t kv_base = (size_t)seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0 * D;
   const T* Kh = K + kv_base;
   const T* Vh = V + kv_base;
   const int q0 = qt * C::BR;
+  if (q0 >= N) return;  // a tile past a shorter packed sequence
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
 
@@ -414,8 +421,8 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
       gf[c] = load16(dO + off + c * 2 * CH);
     }
   }
-  const float lse2 = LSE[(size_t)bh * N + qc] * kLog2e;
-  const float dl = Delta[(size_t)bh * N + qc];
+  const float lse2 = LSE[sq.row0 + qc] * kLog2e;
+  const float dl = Delta[sq.row0 + qc];
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int n_kt = (kv_end + BC - 1) / BC;
@@ -547,9 +554,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
                                                                const float* __restrict__ Lse2,
                                                                const float* __restrict__ Delta,
                                                                T* __restrict__ dK, T* __restrict__ dV,
-                                                               int N, int BHkv, float sl2, float scale, int H,
+                                                               int Nmax, int BHkv, float sl2, float scale, int H,
                                                                int G, int S, float* __restrict__ PartK,
-                                                               float* __restrict__ PartV) {
+                                                               float* __restrict__ PartV, const int* __restrict__ cu,
+                                                               int Ttot, long long kv_rows) {
   using namespace d128;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) T Vs[BC * ROWE];         // 32 KB
@@ -562,10 +570,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
   const int lin = blockIdx.x;
   const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
   const int sp = (lin % (BHkv * S)) / BHkv;  // which 1/S of the group's query heads
-  const int bhk = lin % BHkv;  // key/value head; it serves query heads bh0 .. bh0 + G - 1
-  const int gpw = G / S;       // query heads walked by this workgroup
-  const int bh0 = (bhk / (H / G)) * H + (bhk % (H / G)) * G + sp * gpw;
-  const size_t base = (size_t)bhk * N * D;
+  const int bhk = lin % BHkv;  // (sequence, key/value head)
+  const int gpw = G / S;       // query heads walked by this workgroup: h0 .. h0 + gpw - 1
+  const int bq = bhk / (H / G), hk = bhk % (H / G);
+  const int h0 = hk * G + sp * gpw;
+  const SeqRows skv = seq_rows(cu, Nmax, Ttot, bq, hk, H / G);
+  const int N = skv.n;  // this sequence's length
+  const size_t base = (size_t)skv.row0 * D;
+  if (kt * BC >= N) return;  // a tile past a shorter packed sequence
   const T* Vh = V + base;
   const int kv0 = kt * BC;
   const int kw = kv0 + 32 * w;  // first key of this wave
@@ -711,11 +723,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
   // The walk is repeated for each query head that shares these keys
   // (grouped-query attention), accumulating into the same dK, dV.
   for (int g = 0; g < gpw; ++g) {
-    const int bh = bh0 + g;
-    rq = make_rsrc(Q + (size_t)bh * N * D, (unsigned)N * D * 2);
-    rdo = make_rsrc(dO + (size_t)bh * N * D, (unsigned)N * D * 2);
-    lseh = Lse2 + (size_t)bh * N;
-    dlh = Delta + (size_t)bh * N;
+    const long long qrow0 = seq_rows(cu, Nmax, Ttot, bq, h0 + g, H).row0;
+    rq = make_rsrc(Q + (size_t)qrow0 * D, (unsigned)N * D * 2);
+    rdo = make_rsrc(dO + (size_t)qrow0 * D, (unsigned)N * D * 2);
+    lseh = Lse2 + qrow0;
+    dlh = Delta + qrow0;
     issue(0, 0);
     wait_vmem();
     __syncthreads();
@@ -726,10 +738,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
   }
 
   if (S > 1) {
-    // One of S partial sums over the group: fp32 rows of [S][B, Hkv, N, d],
-    // dK already scaled; bwd_dkdv_reduce_kernel adds them up.
+    // One of S partial sums over the group: fp32 rows of [S][kv_rows, d]
+    // (kv_rows = the rows of dK), dK already scaled; bwd_dkdv_reduce_kernel
+    // adds them up.
     if (kj < N) {
-      const size_t row = ((size_t)sp * BHkv + bhk) * N + kj;
+      const size_t row = (size_t)sp * kv_rows + skv.row0 + kj;
       float* pk = PartK + row * D;
       float* pv = PartV + row * D;
 #pragma unroll
@@ -789,8 +802,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
                                                               const T* __restrict__ dO,
                                                               const float* __restrict__ Lse2,
                                                               const float* __restrict__ Delta,
-                                                              T* __restrict__ dQ, int N, int BH, int num_qt,
-                                                              float sl2, float scale, int H, int G) {
+                                                              T* __restrict__ dQ, int Nmax, int BH, int num_qt,
+                                                              float sl2, float scale, int H, int G,
+                                                              const int* __restrict__ cu, int Ttot) {
   using namespace tiles;
   constexpr int D = 128, KB = 32, BLK_E = KB * 128, CH = 8, DCH = D / 16, NB = D / 32;
   constexpr int QB = 128;           // query rows per workgroup (4 waves x 32)
@@ -804,13 +818,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
   const int lin = blockIdx.x;
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
-  const size_t base = (size_t)bh * N * D;
+  const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
+  const int N = sq.n;  // this sequence's length
+  const size_t base = (size_t)sq.row0 * D;
   const int q0 = qt * QB;
+  if (q0 >= N) return;  // a tile past a shorter packed sequence
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
   // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
   // q = 4w + u, rows 4(q%8)..+3 of the block.
-  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_head(bh, H, G) * N * D, (unsigned)N * D * 2);
+  const long long kv_row0 = seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0;
+  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_row0 * D, (unsigned)N * D * 2);
   T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
 
   const int kv_end = CAUSAL ? min(N, q0 + QB) : N;
@@ -861,8 +879,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
       gf[c] = load16(dO + off + c * 2 * CH);
     }
   }
-  const float lse2 = Lse2[(size_t)bh * N + qc];
-  const float dl = Delta[(size_t)bh * N + qc];
+  const float lse2 = Lse2[sq.row0 + qc];
+  const float dl = Delta[sq.row0 + qc];
 #pragma unroll
   for (int b = 0; b < PF; ++b)
     if (b < nb) issue(b, b);
@@ -955,13 +973,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
 // Sums of the S partial dK (blockIdx.y = 0) and dV (1) of a split
 // grouped-query dK/dV stage, in the fixed order s = 0 .. S-1, rounded once
 // to the output type: 4 elements per thread; n (elements per tensor) is a
-// multiple of 4 since d is.
+// multiple of 4 since d is.  For a packed ragged batch (cu != null, rows of
+// T per head, D elements per row) rows outside [cu[0], cu[B]) of a head
+// belong to no sequence and are left alone.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ PartK,
                                                               const float* __restrict__ PartV, T* __restrict__ dK,
-                                                              T* __restrict__ dV, long long n, int S) {
+                                                              T* __restrict__ dV, long long n, int S,
+                                                              const int* __restrict__ cu, int B, int Ttot, int D) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
+  if (cu != nullptr) {
+    const int t = (int)((i / D) % Ttot);
+    const int lo = min(max(cu[0], 0), Ttot), hi = min(max(cu[B], lo), Ttot);
+    if (t < lo || t >= hi) return;
+  }
   const float* Part = blockIdx.y ? PartV : PartK;
   T* Out = blockIdx.y ? dV : dK;
   f32x4 acc = *reinterpret_cast<const f32x4*>(Part + i);
@@ -974,7 +1000,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
   const int BHkv = a.B * a.Hkv;  // dK/dV workgroups run over key/value heads
   const int G = a.H / a.Hkv;     // query heads per key/value head
-  const long long rows = (long long)BH * a.N;
+  // Rows of the query-side and key-side tensors: [B, H, N] / [B, Hkv, N],
+  // or [H, T] / [Hkv, T] for a packed ragged batch.
+  const long long rows = a.cu ? (long long)a.H * a.T : (long long)BH * a.N;
+  const long long kv_rows = a.cu ? (long long)a.Hkv * a.T : (long long)BHkv * a.N;
   const float sl2 = a.scale * kLog2e;
   if (stage == 1) {
     constexpr int RPB = 256 / (D / Elt<T>::CH);
@@ -988,18 +1017,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BHkv;
       if (blocks * a.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
       const int S = a.splits;
-      const long long n = (long long)BHkv * a.N * D;  // elements of dK (and of dV)
+      const long long n = kv_rows * D;  // elements of dK (and of dV)
       float* part_k = a.part;
       float* part_v = a.part + align256((size_t)S * n * sizeof(float)) / sizeof(float);
       hipLaunchKernelGGL((bwd_dkdv_d128_kernel<T, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                          static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse2, a.delta,
                          static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G,
-                         S, part_k, part_v);
+                         S, part_k, part_v, a.cu, a.T, kv_rows);
       if (S > 1) {
         const unsigned rb = (unsigned)((n / 4 + 255) / 256);
         hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,
-                           static_cast<T*>(a.dk), static_cast<T*>(a.dv), n, S);
+                           static_cast<T*>(a.dk), static_cast<T*>(a.dv), n, S, a.cu, a.B, a.T, D);
       }
       return hipGetLastError();
     }
@@ -1010,7 +1039,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       hipLaunchKernelGGL((bwd_dq_d128_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                          static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse2, a.delta,
-                         static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G);
+                         static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T);
       return hipGetLastError();
     }
   }
@@ -1021,7 +1050,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
-                       a.N, BHkv, sl2, a.scale, a.H, G);
+                       a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T);
     return hipGetLastError();
   }
   if (stage == 3) {
@@ -1032,7 +1061,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dq), a.N, BH, num_qt, sl2,
-                       a.scale, a.H, G);
+                       a.scale, a.H, G, a.cu, a.T);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -248,6 +248,31 @@ __device__ __forceinline__ void write_transposed4<_Float16>(_Float16* tile, int 
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Where the rows of one (sequence, head) live.  Fixed-length batches
+// ([B, heads, N, d], cu == nullptr): head (b, h) starts at row
+// (b*heads + h)*N and has N rows.  Packed ragged batches ([heads, T, d] with
+// sequence offsets cu[0..B]): it starts at row h*T + cu[b] and has
+// cu[b+1] - cu[b] rows.  Offsets are clamped to [0, T] and the length to
+// Nmax, so inconsistent offsets give wrong rows but never an access outside
+// the tensors.
+struct SeqRows {
+  long long row0;
+  int n;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int* cu, int Nmax, int T, int b, int h, int heads) {
+  SeqRows r;
+  if (cu == nullptr) {
+    r.row0 = ((long long)b * heads + h) * Nmax;
+    r.n = Nmax;
+  } else {
+    const int s = min(max(cu[b], 0), T);
+    const int e = min(max(cu[b + 1], s), T);
+    r.row0 = (long long)h * T + s;
+    r.n = min(e - s, Nmax);
+  }
+  return r;
+}
+
 // Grouped-query attention: query head bh = b*H + h reads key/value head
 // (b, h / G) of the [B, H/G, N, d] key/value tensors (G = 1: plain
 // multi-head attention).  Returns that head's index b*(H/G) + h/G.

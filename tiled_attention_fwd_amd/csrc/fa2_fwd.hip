@@ -64,8 +64,9 @@ struct FwdTile {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
-                                                     float* __restrict__ LSE, int N, int BH, int num_qt,
-                                                     float sl2, int H, int G) {
+                                                     float* __restrict__ LSE, int Nmax, int BH, int num_qt,
+                                                     float sl2, int H, int G, const int* __restrict__ cu,
+                                                     int Ttot) {
   using C = FwdTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -76,12 +77,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   const int lin = blockIdx.x;
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
-  const size_t base = (size_t)bh * N * D;
-  const size_t kv_base = (size_t)kv_head(bh, H, G) * N * D;
+  const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
+  const int N = sq.n;  // this sequence's length
+  const size_t base = (size_t)sq.row0 * D;
+  const size_t kv_base = (size_t)seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0 * D;
   const T* Qh = Q + base;
   const T* Kh = K + kv_base;
   const T* Vh = V + kv_base;
   const int q0 = qt * C::BR;
+  if (q0 >= N) return;         // a tile past a shorter packed sequence
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
 
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
                     o[b][4 * g + 3] * inv);
       }
     }
-    if (h == 0) LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+    if (h == 0) LSE[sq.row0 + qi] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -257,8 +261,9 @@ constexpr int BLK_E = KB * ROWE;
 template <typename T, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, T* __restrict__ O,
-                                                        float* __restrict__ LSE, int N, int BH, int num_qt,
-                                                        float sl2, int H, int G) {
+                                                        float* __restrict__ LSE, int Nmax, int BH, int num_qt,
+                                                        float sl2, int H, int G, const int* __restrict__ cu,
+                                                        int Ttot) {
   using namespace tiles;
   constexpr int D = fpp::D, KB = fpp::KB, BLK_E = fpp::BLK_E;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
@@ -272,14 +277,18 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
   const int lin = blockIdx.x;
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
-  const size_t base = (size_t)bh * N * D;
+  const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
+  const int N = sq.n;  // this sequence's length
+  const size_t base = (size_t)sq.row0 * D;
   const T* Qh = Q + base;
   const int q0 = qt * fpp::BR;
+  if (q0 >= N) return;  // a tile past a shorter packed sequence
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
   // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
   // q = 4w + u, rows 4(q%8)..+3 of the block.
-  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_head(bh, H, G) * N * D, (unsigned)N * D * 2);
+  const long long kv_row0 = seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0;
+  const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_row0 * D, (unsigned)N * D * 2);
   T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
 
   const int kv_end = CAUSAL ? min(N, q0 + fpp::BR) : N;
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
                   o[b][4 * g + 3] * inv);
       }
     }
-    if (h == 0) LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+    if (h == 0) LSE[sq.row0 + qi] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -455,7 +464,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fwd_pp_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, a.scale * kLog2e, a.H, a.H / a.Hkv);
+                       static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, a.scale * kLog2e, a.H, a.H / a.Hkv, a.cu,
+                       a.T);
     return hipGetLastError();
   }
   using C = FwdTile<T, D>;
@@ -466,7 +476,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   const float sl2 = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv);
+                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T);
   return hipGetLastError();
 }
 

@@ -25,6 +25,11 @@ struct FwdArgs {
   bool causal;
   int dtype;
   hipStream_t stream;
+  // Packed ragged batch: device sequence offsets [B + 1] (null: fixed length
+  // N, layout [B, H, N, d]); with them the layout is [H, T, d] and N is the
+  // longest sequence.
+  const int* cu;
+  int T;
 };
 
 struct BwdArgs {
@@ -47,6 +52,8 @@ struct BwdArgs {
   float* part;   // splits > 1: fp32 partial dK then dV, [splits][B, Hkv, N, d] each
   int splits;    // workgroups that share one key/value head's query-head group
   hipStream_t stream;
+  const int* cu;  // as FwdArgs
+  int T;
 };
 
 // Workspace layout: D = rowsum(dO * O), then LSE * log2(e), each float
@@ -72,8 +79,9 @@ inline int dkdv_splits(int B, int Hkv, int G, int N, int d, int dtype) {
   }
   return S;
 }
-inline size_t ws_part_bytes(int B, int Hkv, int N, int d, int S) {
-  return S > 1 ? 2 * align256((size_t)S * B * Hkv * N * d * sizeof(float)) : 0;
+// kv_rows: rows of dK ([B, Hkv, N] or, packed, [Hkv, T]).
+inline size_t ws_part_bytes(long long kv_rows, int d, int S) {
+  return S > 1 ? 2 * align256((size_t)S * kv_rows * d * sizeof(float)) : 0;
 }
 
 // Decoding (bf16 or fp16, d = 128): N_q queries [B, H, N_q, d] against a cache

@@ -162,3 +162,88 @@ def make_decode_inputs(w: DecodeWorkload, seed: int | None = None, device: str |
             t = t.to(device)
         out.append(t)
     return tuple(out)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed ragged batch: sequences of the given lengths, one after the
+    other along the token axis of every head ([H, T, d] tensors), with T rows
+    per head (T >= the total length; rows past it belong to no sequence)."""
+    name: str
+    lengths: tuple
+    H: int
+    H_kv: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    qk_mult: float = 1.0
+    T: int = 0  # 0: the total length
+
+    @property
+    def total(self) -> int:
+        return self.T or sum(self.lengths)
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.lengths) if self.lengths else 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return TORCH_DTYPES[self.dtype]
+
+    def cu_seqlens(self) -> list:
+        cu = [0]
+        for n in self.lengths:
+            cu.append(cu[-1] + n)
+        return cu
+
+    def describe(self) -> str:
+        return "%s %d seqs (max %d, T %d) H%d/kv%d d%d %s %s" % (
+            self.name, len(self.lengths), self.max_seqlen, self.total, self.H, self.H_kv, self.d, self.dtype,
+            "causal" if self.causal else "non-causal")
+
+
+def varlen_lengths(count: int, lo: int, hi: int, seed: int) -> tuple:
+    """Sequence lengths drawn uniformly from [lo, hi] by a seeded CPU generator."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (count,), generator=g))
+
+
+# 16 sequences of 512 .. 4096 tokens (seeded), 16 heads, d = 128, causal
+# bf16: the large workload's head shape with a length mix instead of one N.
+VARLEN_WORKLOADS = {
+    "varlen_causal_bf16": VarlenWorkload("varlen_causal_bf16", varlen_lengths(16, 512, 4096, 8), 16, 16, 128,
+                                         "bf16", True, 8),
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload, seed: int | None = None, device: str | torch.device = "cpu"):
+    """Return (q, k, v, dO, cu_seqlens) for a packed workload: q, dO [H, T, d],
+    k, v [H_kv, T, d] in its dtype, cu_seqlens int32 [B + 1]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else int(seed))
+    T = w.total
+    q = torch.randn((w.H, T, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.H_kv, T, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.H_kv, T, w.d), generator=g, dtype=torch.float32)
+    dO = torch.randn((w.H, T, w.d), generator=g, dtype=torch.float32)
+    if w.qk_mult != 1.0:
+        q = q * w.qk_mult
+        k = k * w.qk_mult
+    out = []
+    for t in (q, k, v, dO):
+        t = t.to(w.torch_dtype).contiguous()
+        if str(device) != "cpu":
+            t = t.to(device)
+        out.append(t)
+    cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32)
+    if str(device) != "cpu":
+        cu = cu.to(device)
+    out.append(cu)
+    return tuple(out)

@@ -19,6 +19,7 @@ bounded sample of heads of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 1..7]
     python bench.py --decode decode_gqa_bf16
+    python bench.py --varlen varlen_causal_bf16
 
 Workload 6 is the same shape with grouped-query attention (16 query heads
 over 2 key/value heads) and workload 7 the same shape in fp16; their lines
@@ -235,6 +236,77 @@ def bench_decode(args) -> int:
     return 0
 
 
+def bench_varlen(args) -> int:
+    """One step of a packed ragged batch: fa2_forward_varlen and the three
+    backward stages; counted FLOP summed over the sequences (4 H n^2 d per
+    sequence forward, halved when causal; backward 2.5x, step 3.5x)."""
+    import torch
+    import tiled_attention_fwd_amd as fa
+    import workloads
+
+    w = workloads.VARLEN_WORKLOADS[args.varlen]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, dO, cu = workloads.make_varlen_inputs(w, seed=args.seed, device=dev)
+    H, T, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B = len(w.lengths)
+    ws = torch.empty(max(fa.fa2_backward_workspace_size_varlen(B, H, w.H_kv, T, w.max_seqlen, d, q.dtype), 16),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.fa2_forward_varlen(q, k, v, o, lse, cu, w.max_seqlen, w.causal, w.scale, stream)
+        for s in (1, 2, 3):
+            if evs:
+                evs[s].record(stream)
+            fa.fa2_backward_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu, w.max_seqlen, w.causal, w.scale, ws,
+                                   stream, stage=s)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(events[s])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    names = ["fwd_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    mean_ms = {n: statistics.fmean(events[s][i].elapsed_time(events[s][i + 1]) for s in range(K))
+               for i, n in enumerate(names)}
+    fwd_f = sum(4.0 * H * n * n * d * (0.5 if w.causal else 1.0) for n in w.lengths)
+    step_f = 3.5 * fwd_f
+    peak = PEAK_TFLOPS[w.dtype]
+    value = step_f / (ms_per_step * 1e-3) / 1e12
+    kflop = {"fwd_kernel": fwd_f, "bwd_dkdv_kernel": 0.8 * 2.5 * fwd_f, "bwd_dq_kernel": 0.2 * 2.5 * fwd_f}
+    dom = max(kflop, key=lambda n: mean_ms[n])
+    achieved = kflop[dom] / (mean_ms[dom] * 1e-3) / 1e12
+    result = {
+        "metric": "attention fwd+bwd TFLOP/s, packed ragged batch (bf16 16 seqs of 512-4096, H16 d128 causal)",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "lengths": list(w.lengths), "H": H, "H_kv": w.H_kv, "T": T, "d": d,
+                   "causal": w.causal, "seed": w.seed if args.seed is None else args.seed},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "mean_launch_ms": mean_ms[dom],
+                     "flop_per_launch": kflop[dom]},
+        "cpu_baseline": None,
+        "detail": {"kernel_ms": mean_ms, "step_frac_peak": value / peak},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +317,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--decode", default=None, metavar="NAME",
                     help="time decoding on a named decoding workload instead (decode_gqa_bf16)")
+    ap.add_argument("--varlen", default=None, metavar="NAME",
+                    help="time a packed ragged batch instead (varlen_causal_bf16)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to scale HBM byte counters")
     args = ap.parse_args()
@@ -271,6 +345,8 @@ def main() -> int:
         return 0
     if args.decode:
         return bench_decode(args)
+    if args.varlen:
+        return bench_varlen(args)
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

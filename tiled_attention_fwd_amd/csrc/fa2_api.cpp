@@ -32,24 +32,6 @@ bool is_empty(int B, int H, int N) { return B == 0 || H == 0 || N == 0; }
 // Key/value heads: 1 <= H_kv, and H_kv divides H (both may be 0 when H is).
 bool valid_hkv(int H, int H_kv) { return H == 0 ? H_kv >= 0 : (H_kv >= 1 && H % H_kv == 0); }
 
-}  // namespace
-
-extern "C" {
-
-const char* fa2_status_string(int status) {
-  switch (status) {
-    case FA2_OK: return "FA2_OK";
-    case FA2_ERR_INVALID_ARG: return "FA2_ERR_INVALID_ARG: null pointer, negative size, bad scale or dtype, or size overflow";
-    case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED: head dim not in {16,32,64,128} or pointer not 16-byte aligned";
-    case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: backward workspace missing or too small";
-    case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: a HIP kernel launch failed";
-    default: return "unknown fa2 status";
-  }
-}
-
-}  // extern "C"
-
-namespace {
 
 // Packed ragged batches: T rows per head, sequences of at most max_seqlen
 // rows (the grid's length), device offsets cu[0..B].
@@ -72,36 +54,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA2_ERR_UNSUPPORTED;
-  fa2::FwdArgs a{q,     k,           v,     o, lse, B, H, N, d, H_kv, scale, causal != 0, dtype,
-                 static_cast<hipStream_t>(stream), cu, T};
+  fa2::FwdArgs a{q, k, v, o, lse, B, H, N, d, H_kv, scale, causal != 0, dtype, static_cast<hipStream_t>(stream),
+                 cu, T};
   return fa2::launch_forward(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
-
-}  // namespace
-
-extern "C" {
-
-int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
-                   int N, int d, float scale, int causal, int dtype, void* stream) {
-  return forward_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, dtype, nullptr, 0, stream);
-}
-
-int fa2_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
-                       int B, int H, int H_kv, int T, int max_seqlen, int d, float scale, int causal, int dtype,
-                       void* stream) {
-  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
-  if (st != FA2_OK) return st;
-  return forward_impl(q, k, v, o, lse, B, H, H_kv, max_seqlen, d, scale, causal, dtype, cu_seqlens, T, stream);
-}
-
-int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                float scale, int causal, int dtype, void* stream) {
-  return fa2_forward_ex(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
-}
-
-}  // extern "C"
-
-namespace {
 
 // Workspace of a backward whose query side has `rows` rows and key side
 // `kv_rows` ([B, H, N] and [B, H_kv, N], or [H, T] and [H_kv, T]).
@@ -110,31 +66,11 @@ size_t ws_bytes(int B, int H, int H_kv, int N, int d, int dtype, long long rows,
   return fa2::ws_total_bytes((size_t)rows, d, dtype) + fa2::ws_part_bytes(kv_rows, d, S);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fa2_backward_workspace_size_ex(int B, int H, int H_kv, int N, int d, int dtype) {
-  if (check_sizes(B, H, N, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
-  if (is_empty(B, H, N)) return 0;
-  return ws_bytes(B, H, H_kv, N, d, dtype, (long long)B * H * N, (long long)B * H_kv * N);
-}
-
-size_t fa2_backward_workspace_size_varlen(int B, int H, int H_kv, int T, int max_seqlen, int d, int dtype) {
-  if (check_sizes(B, H, max_seqlen, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
-  if (T < 0 || max_seqlen > T || (int64_t)T * d >= ((int64_t)1 << 31)) return 0;
-  if (is_empty(B, H, max_seqlen)) return 0;
-  return ws_bytes(B, H, H_kv, max_seqlen, d, dtype, (long long)H * T, (long long)H_kv * T);
-}
-
-size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
-  return fa2_backward_workspace_size_ex(B, H, H, N, d, dtype);
-}
-
-static int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v,
-                         const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
-                         int H, int H_kv, int N, int d, float scale, int causal, int dtype, void* workspace,
-                         size_t workspace_bytes, void* stream, const int* cu = nullptr, int T = 0) {
+// Stages stage_first .. stage_last of the backward; N as in forward_impl.
+int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v, const void* o,
+                  const void* dO, const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N,
+                  int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                  const int* cu = nullptr, int T = 0) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
@@ -154,12 +90,68 @@ static int backward_impl(int stage_first, int stage_last, const void* q, const v
   float* part = static_cast<float*>(static_cast<void*>(static_cast<char*>(workspace) +
                                                        fa2::ws_total_bytes(rows, d, dtype)));
   const int splits = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
-  fa2::BwdArgs a{q,  k, v, o,     dO,          lse,   dq,    dk,   dv,     B,     H,
-                 N,  d, H_kv, scale, causal != 0, dtype, delta, lse2, part, splits,
-                 static_cast<hipStream_t>(stream), cu, T};
+  fa2::BwdArgs a{q,     k,     v,    o,    dO,     lse,   dq, dk, dv, B, H, N, d, H_kv, scale, causal != 0,
+                 dtype, delta, lse2, part, splits, static_cast<hipStream_t>(stream), cu, T};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa2_status_string(int status) {
+  switch (status) {
+    case FA2_OK: return "FA2_OK";
+    case FA2_ERR_INVALID_ARG: return "FA2_ERR_INVALID_ARG: null pointer, negative size, bad scale or dtype, or size overflow";
+    case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED: head dim not in {16,32,64,128} or pointer not 16-byte aligned";
+    case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: a HIP kernel launch failed";
+    default: return "unknown fa2 status";
+  }
+}
+
+int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, int dtype, void* stream) {
+  return fa2_forward_ex(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
+}
+
+int fa2_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                   int N, int d, float scale, int causal, int dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, dtype, nullptr, 0, stream);
+}
+
+int fa2_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                       int B, int H, int H_kv, int T, int max_seqlen, int d, float scale, int causal, int dtype,
+                       void* stream) {
+  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
+  if (st != FA2_OK) return st;
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, max_seqlen, d, scale, causal, dtype, cu_seqlens, T, stream);
+}
+
+size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype) {
+  return fa2_backward_workspace_size_ex(B, H, H, N, d, dtype);
+}
+
+size_t fa2_backward_workspace_size_ex(int B, int H, int H_kv, int N, int d, int dtype) {
+  if (check_sizes(B, H, N, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
+  if (is_empty(B, H, N)) return 0;
+  return ws_bytes(B, H, H_kv, N, d, dtype, (long long)B * H * N, (long long)B * H_kv * N);
+}
+
+size_t fa2_backward_workspace_size_varlen(int B, int H, int H_kv, int T, int max_seqlen, int d, int dtype) {
+  if (check_sizes(B, H, max_seqlen, d, dtype) != FA2_OK || !valid_hkv(H, H_kv)) return 0;
+  if (T < 0 || max_seqlen > T || (int64_t)T * d >= ((int64_t)1 << 31)) return 0;
+  if (is_empty(B, H, max_seqlen)) return 0;
+  return ws_bytes(B, H, H_kv, max_seqlen, d, dtype, (long long)H * T, (long long)H_kv * T);
+}
+
+int fa2_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, workspace,
+                         workspace_bytes, stream);
 }
 
 int fa2_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -169,11 +161,21 @@ int fa2_backward_ex(const void* q, const void* k, const void* v, const void* o, 
                        workspace_bytes, stream);
 }
 
-int fa2_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
-                 void* workspace, size_t workspace_bytes, void* stream) {
-  return fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, workspace,
-                         workspace_bytes, stream);
+int fa2_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int B, int H,
+                        int H_kv, int T, int max_seqlen, int d, float scale, int causal, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
+  if (st != FA2_OK) return st;
+  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal, dtype,
+                       workspace, workspace_bytes, stream, cu_seqlens, T);
+}
+
+int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dO,
+                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                       int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa2_backward_stage_ex(stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, scale, causal, dtype,
+                               workspace, workspace_bytes, stream);
 }
 
 int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -185,11 +187,16 @@ int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v
                        workspace, workspace_bytes, stream);
 }
 
-int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dO,
-                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                       int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return fa2_backward_stage_ex(stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, scale, causal, dtype,
-                               workspace, workspace_bytes, stream);
+int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int B, int H, int H_kv, int T, int max_seqlen, int d,
+                              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
+  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
+  if (st != FA2_OK) return st;
+  return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal,
+                       dtype, workspace, workspace_bytes, stream, cu_seqlens, T);
 }
 
 size_t fa2_decode_workspace_size(int B, int H, int H_kv, int N_q, int N_k, int d, int dtype) {
@@ -223,28 +230,6 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   fa2::DecArgs a{q,     k,           v,     o,     lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0,
                  dtype, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
   return fa2::launch_decode(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
-}
-
-int fa2_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                        const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int B, int H,
-                        int H_kv, int T, int max_seqlen, int d, float scale, int causal, int dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
-  if (st != FA2_OK) return st;
-  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal, dtype,
-                       workspace, workspace_bytes, stream, cu_seqlens, T);
-}
-
-int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const void* v, const void* o,
-                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
-                              const int* cu_seqlens, int B, int H, int H_kv, int T, int max_seqlen, int d,
-                              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
-  const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
-  if (st != FA2_OK) return st;
-  return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal,
-                       dtype, workspace, workspace_bytes, stream, cu_seqlens, T);
 }
 
 }  // extern "C"

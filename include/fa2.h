@@ -207,14 +207,15 @@ int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const voi
  *   q, o   [B, H, N_q, d] (dtype); k, v [B, H_kv, N_k, d] (dtype), H_kv
  *          dividing H, query head h reading key/value head h / (H / H_kv);
  *   lse    [B, H, N_q] float, natural log, as fa2_forward.
- * Arithmetic as fa2_forward in the 16-bit modes.  The cache is split into chunks
- * walked by separate workgroups; a second kernel merges their normalised
- * partial outputs with weights exp(LSE_chunk - max) and rounds O once.  The
- * split depends only on the sizes, so results are the same bits from run to
- * run.
- * Supported: dtype FA2_BF16 or FA2_F16 with d = 128 (else FA2_ERR_UNSUPPORTED, after the
- * argument checks).  N_k = 0 with N_q > 0, or causal with N_q > N_k:
- * FA2_ERR_INVALID_ARG.  B, H or N_q = 0: no-op.
+ * Arithmetic as fa2_forward.  For FA2_BF16 and FA2_F16 with d = 128 the
+ * cache is split into chunks walked by separate workgroups, and a second
+ * kernel merges their normalised partial outputs with weights
+ * exp(LSE_chunk - max) and rounds O once; the split depends only on the
+ * sizes, so results are the same bits from run to run.  Every other
+ * supported type and head size (as fa2_forward) runs the forward kernel with
+ * the cache as its keys, unsplit.
+ * N_k = 0 with N_q > 0, or causal with N_q > N_k: FA2_ERR_INVALID_ARG.
+ * B, H or N_q = 0: no-op.
  * workspace: device memory of at least fa2_decode_workspace_size(...) bytes,
  * 16-byte aligned (the partial results); may be NULL when that size is 0.
  * Asynchronous on stream, like the other calls.

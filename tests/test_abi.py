@@ -215,9 +215,9 @@ def dec(L, B=1, H=4, H_kv=2, Nq=1, Nk=100, d=128, scale=0.125, causal=0, dtype=1
     (dict(H_kv=0), fa.FA2_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA2_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA2_ERR_INVALID_ARG), (dict(dtype=5), fa.FA2_ERR_INVALID_ARG),
     (dict(Nk=0), fa.FA2_ERR_INVALID_ARG), (dict(Nq=5, Nk=4, causal=1), fa.FA2_ERR_INVALID_ARG),
-    (dict(dtype=0), fa.FA2_ERR_UNSUPPORTED), (dict(d=64), fa.FA2_ERR_UNSUPPORTED),
-    (dict(dtype=3), fa.FA2_ERR_INVALID_ARG), (dict(d=64, dtype=2), fa.FA2_ERR_UNSUPPORTED),
-    (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(ptr=None), fa.FA2_ERR_INVALID_ARG),
+    (dict(dtype=3), fa.FA2_ERR_INVALID_ARG), (dict(d=48, dtype=0), fa.FA2_ERR_UNSUPPORTED),
+    (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(d=256, dtype=2), fa.FA2_ERR_UNSUPPORTED),
+    (dict(ptr=None), fa.FA2_ERR_INVALID_ARG), (dict(ptr=None, dtype=0, d=64), fa.FA2_ERR_INVALID_ARG),
     (dict(ptr=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(Nk=1 << 24), fa.FA2_ERR_INVALID_ARG),
 ])
 def test_decode_rejects(L, kw, status):

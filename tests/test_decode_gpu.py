@@ -6,8 +6,9 @@ Same error measure and limits as the forward and backward parity tests
 accumulation); outputs are NaN-filled inside canary guard bands before the
 call.  The cases cover the direct path (one chunk) and the split path (a
 partial result per chunk and the merge kernel), ragged caches, more than 32
-rows per key/value head, causal rows that see no key of a chunk, and the
-full-size decoding workload on sampled heads.
+rows per key/value head, causal rows that see no key of a chunk, the
+full-size decoding workload on sampled heads, and the other types and head
+sizes, which run the generic forward kernel (float32 limit 1e-4).
 """
 import pytest
 import torch
@@ -21,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 # bf16 as stated for the method; fp16 derived from it (unit roundoff 2^-11
 # against 2^-8: 2e-2 * 2^-3).
-TOL = {"bf16": 2e-2, "f16": 2.5e-3}
+TOL = {"bf16": 2e-2, "f16": 2.5e-3, "f32": 1e-4}
 
 
 def gpu_decode(q, k, v, causal, scale):
@@ -93,6 +94,24 @@ def test_decode_parity_f16(B, H, H_kv, Nq, Nk, causal):
     run_decode_case(dw(B, H, H_kv, Nq, Nk, causal, seed, "f16"))
 
 
+# Other types and head sizes: the generic forward kernel with the cache as
+# its keys (no split).
+GENERIC_CASES = [
+    (2, 4, 2, 1, 700, 64, "bf16", False),
+    (1, 6, 3, 5, 300, 64, "f16", True),
+    (2, 2, 1, 3, 129, 32, "f32", True),
+    (1, 3, 3, 16, 16, 16, "f32", True),
+    (1, 8, 2, 40, 1000, 128, "f32", False),
+    (1, 2, 2, 200, 70, 64, "bf16", False),  # more queries than keys, no mask
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,Nq,Nk,d,dtype,causal", GENERIC_CASES)
+def test_decode_parity_generic(B, H, H_kv, Nq, Nk, d, dtype, causal):
+    seed = 4300 + 7 * B + 13 * H + H_kv + 31 * Nq + Nk + d + (1 if causal else 0)
+    run_decode_case(workloads.DecodeWorkload("decode", B, H, H_kv, Nq, Nk, d, dtype, causal, seed))
+
+
 def test_decode_workload_sampled_heads():
     """The decoding workload at full size (16 sequences, 64 query heads over
     8 key/value heads, one query against a 16 K cache), as the benchmark
@@ -125,10 +144,6 @@ def test_decode_rejects_on_gpu():
     k = torch.zeros((1, 2, 3, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.Fa2Error):  # causal with more queries than keys
         fa.decode(q, k, k, True)
-    q64 = torch.zeros((1, 2, 1, 64), dtype=torch.float16, device="cuda")
-    with pytest.raises(fa.Fa2Error):  # only d = 128 is provided
-        fa.decode(q64, q64, q64, False)
-    q32 = torch.zeros((1, 2, 1, 128), dtype=torch.float32, device="cuda")
-    k32 = torch.zeros((1, 2, 8, 128), dtype=torch.float32, device="cuda")
-    with pytest.raises(fa.Fa2Error):  # float32 decoding is not provided
-        fa.decode(q32, k32, k32, False)
+    q48 = torch.zeros((1, 2, 1, 48), dtype=torch.float16, device="cuda")
+    with pytest.raises(fa.Fa2Error):  # head size outside 16, 32, 64, 128
+        fa.decode(q48, q48, q48, False)

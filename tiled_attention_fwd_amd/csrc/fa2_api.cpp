@@ -33,6 +33,11 @@ bool is_empty(int B, int H, int N) { return B == 0 || H == 0 || N == 0; }
 bool valid_hkv(int H, int H_kv) { return H == 0 ? H_kv >= 0 : (H_kv >= 1 && H % H_kv == 0); }
 
 
+// Decoding splits the cache over workgroups for 16-bit types at d = 128; other
+// types and head sizes run the generic forward kernel, which needs no
+// workspace.
+bool decode_split_path(int dtype, int d) { return (dtype == FA2_BF16 || dtype == FA2_F16) && d == 128; }
+
 // Packed ragged batches: T rows per head, sequences of at most max_seqlen
 // rows (the grid's length), device offsets cu[0..B].
 int check_varlen(const int* cu, int B, int T, int max_seqlen, int d) {
@@ -55,7 +60,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA2_ERR_UNSUPPORTED;
   fa2::FwdArgs a{q, k, v, o, lse, B, H, N, d, H_kv, scale, causal != 0, dtype, static_cast<hipStream_t>(stream),
-                 cu, T};
+                 cu, T, 0};
   return fa2::launch_forward(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
@@ -201,7 +206,7 @@ int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const voi
 
 size_t fa2_decode_workspace_size(int B, int H, int H_kv, int N_q, int N_k, int d, int dtype) {
   if (B <= 0 || H <= 0 || N_q <= 0 || N_k <= 0 || !valid_hkv(H, H_kv)) return 0;
-  if ((dtype != FA2_BF16 && dtype != FA2_F16) || d != 128) return 0;
+  if (!decode_split_path(dtype, d)) return 0;
   if ((int64_t)N_k * d >= ((int64_t)1 << 31) || (int64_t)B * H * N_q >= ((int64_t)1 << 31)) return 0;
   return fa2::decode_ws_bytes(B, H, H_kv, N_q, N_k, d);
 }
@@ -218,10 +223,17 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   if ((int64_t)B * H * N_q >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;
   if (B == 0 || H == 0 || N_q == 0) return FA2_OK;
   if (N_k == 0 || (causal && N_q > N_k)) return FA2_ERR_INVALID_ARG;
-  if ((dtype != FA2_BF16 && dtype != FA2_F16) || d != 128) return FA2_ERR_UNSUPPORTED;
+  if (!supported_d(d)) return FA2_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA2_ERR_UNSUPPORTED;
+  if (!decode_split_path(dtype, d)) {
+    // Other types and head sizes: the generic forward kernel with the cache
+    // as its keys (one workgroup per 128-query tile walks the whole cache).
+    fa2::FwdArgs a{q,     k, v, o, lse, B, H, N_q, d, H_kv, scale, causal != 0, dtype, static_cast<hipStream_t>(stream),
+                   nullptr, 0, N_k};
+    return fa2::launch_forward(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+  }
   const size_t need = fa2::decode_ws_bytes(B, H, H_kv, N_q, N_k, d);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;

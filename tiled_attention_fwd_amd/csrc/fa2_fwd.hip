@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int Nmax, int BH, int num_qt,
                                                      float sl2, int H, int G, const int* __restrict__ cu,
-                                                     int Ttot) {
+                                                     int Ttot, int Nk) {
   using C = FwdTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -78,9 +78,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
   const int bh = lin % BH;
   const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
-  const int N = sq.n;  // this sequence's length
+  const int N = sq.n;  // this sequence's length (query rows)
+  // Keys: the same rows, or (decoding, Nk > 0) a cache of Nk rows per
+  // key/value head whose last N positions are the queries, so with the
+  // causal mask query i keeps keys j <= i + coff.
+  const int Nkv = Nk > 0 ? Nk : N;
+  const int coff = Nkv - N;
+  const long long kv_row0 = Nk > 0 ? ((long long)(bh / H) * (H / G) + (bh % H) / G) * Nk
+                                   : seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0;
   const size_t base = (size_t)sq.row0 * D;
-  const size_t kv_base = (size_t)seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0 * D;
+  const size_t kv_base = (size_t)kv_row0 * D;
   const T* Qh = Q + base;
   const T* Kh = K + kv_base;
   const T* Vh = V + kv_base;
@@ -98,10 +105,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     for (int c = 0; c < C::DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int kv_end = CAUSAL ? min(Nkv, q0 + C::BR + coff) : Nkv;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  // Tile loads: rows past N load row N-1; those keys are masked to -inf, so
+  // Tile loads: rows past Nkv load row Nkv-1; those keys are masked to -inf, so
   // their (finite) values never reach the output.
   u32x4 kr[C::PER_T], vr[C::PER_T];
   auto load_tile = [&](int kt) {
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     for (int u = 0; u < C::PER_T; ++u) {
       const int c = tid + 256 * u;
       if (c < C::CHUNKS) {
-        const size_t off = (size_t)min(kt * BC + c / C::ROW_CH, N - 1) * D + (c % C::ROW_CH) * CH;
+        const size_t off = (size_t)min(kt * BC + c / C::ROW_CH, Nkv - 1) * D + (c % C::ROW_CH) * CH;
         kr[u] = load16(Kh + off);
         vr[u] = load16(Vh + off);
       }
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     const T* vs = Vs[kt & 1];
     const int kb0 = kt * BC;
     // 32-key blocks of this tile that hold a key this wave may see.
-    const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
+    const int last_key = CAUSAL ? min(qw + 31 + coff, Nkv - 1) : Nkv - 1;
     const int nlive = MASKED ? (last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1)) : C::NJB;
 
     f32x16 s[C::NJB];
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = kb + acc_row(r, h);
-            s[jb][r] = ((CAUSAL & (j > qi)) | (j >= N)) ? -INFINITY : s[jb][r];  // a select
+            s[jb][r] = ((CAUSAL & (j > qi + coff)) | (j >= Nkv)) ? -INFINITY : s[jb][r];  // a select
           }
         }
         float mx = s[jb][0];
@@ -209,9 +216,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
   };
-  // Key tiles wholly below every row of this query tile and wholly before N
+  // Key tiles wholly below every row of this query tile and wholly before Nkv
   // need no mask; the diagonal and ragged tiles come last.
-  const int kt_full = min(n_kt, CAUSAL ? min(q0, N) / BC : N / BC);
+  const int kt_full = min(n_kt, CAUSAL ? min(q0 + coff, Nkv) / BC : Nkv / BC);
   int kt = 0;
   for (; kt < kt_full; ++kt) tile(kt, BoolC<false>{});
   for (; kt < n_kt; ++kt) tile(kt, BoolC<true>{});
@@ -458,6 +465,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   if constexpr (sizeof(T) == 2 && D == 128) {
+    if (a.Nk > 0) return hipErrorInvalidValue;  // decoding has its own kernel here
     const int BH = a.B * a.H;
     const int num_qt = (a.N + fpp::BR - 1) / fpp::BR;
     const long long blocks = (long long)num_qt * BH;
@@ -476,7 +484,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   const float sl2 = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T);
+                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T, a.Nk);
   return hipGetLastError();
 }
 

@@ -30,6 +30,10 @@ struct FwdArgs {
   // longest sequence.
   const int* cu;
   int T;
+  // Decoding through the generic kernel: k, v hold Nk rows per key/value
+  // head ([B, Hkv, Nk, d]) and the N queries are their last positions (0: the
+  // keys are the query rows).
+  int Nk;
 };
 
 struct BwdArgs {

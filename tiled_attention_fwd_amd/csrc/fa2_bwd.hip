@@ -893,11 +893,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
     dp = f32x16{};
     const char* kb_ = reinterpret_cast<const char*>(Ks[slot]);
     const char* vb_ = reinterpret_cast<const char*>(Vs[slot]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
       mfma_chunk<T>(s, lds16(kb_, kofs[c]), qf[c]);
       mfma_chunk<T>(dp, lds16(vb_, kofs[c]), gf[c]);
     }
+    // LDS reads run three chunks ahead of the products that use them.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   f32x16 dq[NB];
@@ -925,12 +935,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
       dp[r] = p * (dp[r] - dl);
     }
     const char* kb_ = reinterpret_cast<const char*>(Ks[SLOT]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u32x4 sb = pack_chunk<T>(dp, t);
 #pragma unroll
       for (int b = 0; b < NB; ++b) mfma_chunk<T>(dq[b], tr_frag(kb_, tofs0[b] + t * 4096, tofs1[b] + t * 4096), sb);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
     if (ahead)
       wait_vmem4();
     else

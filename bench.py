@@ -92,6 +92,18 @@ def stored_traffic(kernel: str, workload: str):
     return float(b.group(1))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (for the oracle's timing line)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
     """Time the fp64 oracle (test infrastructure) on whole heads of the same
     workload until about ``budget_s`` seconds of work are done; also report
@@ -129,7 +141,7 @@ def cpu_baseline(w, inputs, gpu_outs, budget_s: float):
     value = step_flop_per_unit * done / t_total / 1e12
     what = "heads" if G == 1 else "key/value heads (x%d query heads)" % G
     return {
-        "value": value, "unit": "TFLOP/s", "cores": orc.max_threads(), "kind": "oracle",
+        "value": value, "unit": "TFLOP/s", "cores": orc.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
         "sample": "%d of %d %s of %s, fp64 forward+backward, %.1f s" % (done, len(units), what, w.name, t_total),
     }, {"units_checked": done, "max_rel_err": errs}
 
@@ -168,7 +180,8 @@ def decode_cpu_baseline(w, inputs, gpu_outs, budget_s: float):
             break
     per_unit = decode_bytes(w) / len(units)
     return {
-        "value": per_unit * done / t_total / 1e9, "unit": "GB/s", "cores": orc.max_threads(), "kind": "oracle",
+        "value": per_unit * done / t_total / 1e9, "unit": "GB/s", "cores": orc.max_threads(),
+        "cpu_model": cpu_model(), "kind": "oracle",
         "sample": "%d of %d key/value heads (x%d query heads) of %s, fp64 decode, %.1f s"
                   % (done, len(units), G, w.name, t_total),
     }, {"units_checked": done, "max_rel_err": err}
@@ -417,7 +430,9 @@ def main() -> int:
                    "seed": w.seed if args.seed is None else args.seed},
         "roofline": roofline,
     }
+    step_ms = sorted(events[s][0].elapsed_time(events[s][4]) for s in range(K))
     detail = {
+        "step_events_median_ms": statistics.median(step_ms), "step_events_min_ms": step_ms[0],
         "fwd": {"ms": mean_ms["fwd_kernel"], "tflops": fwd_f / (mean_ms["fwd_kernel"] * 1e-3) / 1e12},
         "bwd": {"ms": bwd_ms, "tflops": bwd_f / (bwd_ms * 1e-3) / 1e12},
         "step_events_ms": mean_ms["fwd_kernel"] + bwd_ms,

@@ -23,15 +23,21 @@
 //                    dV^T += dO^T P and dK^T += Q^T dS on MFMA, with P and dS
 //                    fed straight from the accumulator layout and Q^T, dO^T
 //                    read from the row-major LDS tiles by transpose reads.
-//                    For bf16 and d = 128, bwd_dkdv_d128_kernel runs the
-//                    same pass with direct-to-LDS loads into swizzled tiles
-//                    and two independent workgroups per CU.
+//                    For bf16 and fp16 at d = 128, bwd_dkdv_d128_kernel
+//                    runs the same pass with direct-to-LDS loads into
+//                    swizzled tiles and two independent workgroups per CU.
+//                    With grouped-query heads a workgroup walks every query
+//                    head of its key/value head's group (or a 1/S share of
+//                    them, bwd_dkdv_reduce_kernel then summing the S fp32
+//                    partials in a fixed order).
 //   bwd_dq_kernel    one workgroup per (batch, head, 128-query tile), shaped
 //                    like the forward pass: S^T = K Q^T and dP^T = V dO^T on
 //                    MFMA, so each lane owns one query and its LSE and D are
-//                    scalars, then dQ^T += K^T dS^T.  For bf16 and d = 128,
-//                    bwd_dq_d128_kernel runs it over a ring of direct-loaded
-//                    32-key blocks, like the bf16 d = 128 forward.
+//                    scalars, then dQ^T += K^T dS^T.  For the 16-bit types
+//                    at d = 128, bwd_dq_d128_kernel runs it over a ring of
+//                    direct-loaded 32-key blocks, like the d = 128 forward.
+// Every kernel takes its (sequence, head) rows from seq_rows, so fixed-length
+// and packed ragged batches share them.
 // The two halves recompute S and dP instead of exchanging dS, so dQ needs no
 // atomics or fp32 accumulator and the result is deterministic.
 // Causal: tiles start and stop at the diagonal, blocks entirely above it
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for bf16 with d = 128: one 4-wave workgroup per (batch, head,
+// dK, dV for the 16-bit types at d = 128: one 4-wave workgroup per (batch, head,
 // 128-key tile), two workgroups per CU, so every SIMD runs two waves from
 // different workgroups whose barriers are independent: one wave's softmax
 // work can overlap the other's MFMAs without the two being held in step.
@@ -790,7 +796,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
   }
 }
 
-// dQ for bf16 and d = 128: the pass of bwd_dq_kernel organised like the bf16
+// dQ for the 16-bit types at d = 128: the pass of bwd_dq_kernel organised like the
 // d = 128 forward.  32-key blocks of K and V reach LDS through direct loads
 // into a ring of 4 slots (unpadded swizzled rows), issued 3 blocks ahead,
 // one barrier per block; lane offsets of every fragment and load are

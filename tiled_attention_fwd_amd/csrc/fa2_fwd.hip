@@ -10,7 +10,12 @@
 // laid out for CDNA4.
 //
 // Two kernels follow: fwd_kernel for every type and head size, and
-// fwd_pp_kernel, a leaner schedule of the same pass for bf16 and d = 128.
+// fwd_pp_kernel, a leaner schedule of the same pass for the 16-bit types
+// (bf16, fp16) at d = 128.  Both serve fixed-length batches ([B, H, N, d]),
+// packed ragged batches ([H, T, d] with sequence offsets) and grouped-query
+// heads; fwd_kernel also serves decoding for the types and head sizes the
+// split-cache decode kernel does not cover (a key length of its own, the
+// queries being the last positions).
 //
 // Workgroup: 4 waves x 32 query rows = a 128-row query tile.  Each wave
 // computes the TRANSPOSED score block S^T = K Q^T (keys x queries) on MFMA,
@@ -33,7 +38,8 @@
 // scale*log2(e) folded into one FMA.  The running max only moves when the
 // block max exceeds it by more than kSlack (base-2 units), so the O rescale
 // is skipped in most tiles; weights are then at most 2^kSlack, harmless in
-// fp32 and bf16.  At the end O = acc / l and LSE = (m + log2 l) * ln 2.
+// fp32 and the 16-bit types.  At the end O = acc / l and
+// LSE = (m + log2 l) * ln 2.
 #include "fa2_common.hpp"
 #include "fa2_launch.hpp"
 #include "fa2_swz.hpp"
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   }
 }
 
-// Forward for bf16 and d = 128.  Same pass as fwd_kernel, organised around
+// Forward for the 16-bit types at d = 128.  Same pass as fwd_kernel, organised around
 // 32-key blocks that reach LDS through direct loads into a ring of 4 block
 // slots (K and V, unpadded swizzled rows), issued 3 blocks ahead, one
 // barrier per block.  Within a wave the score products of block b+1 are

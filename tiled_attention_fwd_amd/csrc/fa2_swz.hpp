@@ -1,6 +1,6 @@
 // fa2_swz.hpp -- swizzled LDS tiles and direct global-to-LDS loads (gfx950).
 //
-// Shared by the forward and backward kernels for bf16 and d = 128, whose
+// Shared by the forward, backward and decode kernels for the 16-bit types at d = 128, whose
 // tiles are stored unpadded, 256 bytes per row, and filled by direct loads
 // (no register staging).
 #pragma once

@@ -328,6 +328,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (replays, no per-kernel events)")
     ap.add_argument("--decode", default=None, metavar="NAME",
                     help="time decoding on a named decoding workload instead (decode_gqa_bf16)")
     ap.add_argument("--varlen", default=None, metavar="NAME",
@@ -443,6 +445,29 @@ def main() -> int:
         detail[kk]["frac_peak"] = detail[kk]["tflops"] / peak
     detail["step_frac_peak"] = value / peak
     detail["source_hash"] = {k: source_hash(k) for k in KERNEL_SOURCES}
+    if args.graph:
+        # The same step captured once in a HIP graph and replayed K times:
+        # what the launch overhead costs the small workloads.
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fwd_call(q, k, v, o, lse, w.causal, w.scale)
+            for st in (1, 2, 3):
+                stage_call(st, q, k, v, o, dO, lse, dq, dk, dv, w.causal, w.scale, ws)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / K
+        detail["graph"] = {"ms_per_step": g_ms, "tflops": step_f / (g_ms * 1e-3) / 1e12}
     if args.cpu_budget > 0:
         cb, parity = cpu_baseline(w, (q, k, v, dO), (o, lse, dq, dk, dv), args.cpu_budget)
         result["cpu_baseline"] = cb

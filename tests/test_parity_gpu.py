@@ -319,3 +319,44 @@ def test_gqa_backward_bitwise_repeatable():
     assert a[1].shape == k.shape and a[2].shape == v.shape
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# Two independent tilings of the 16-bit d = 128 path: the tuned kernels
+# (direct loads into swizzled LDS rings) and the generic ones (register-staged
+# padded tiles), selected by FA2_FORCE_GENERIC.  Both must meet the tolerance
+# against the oracle and agree with each other within it.
+@pytest.mark.parametrize("dtype,H,H_kv,causal", [("bf16", 8, 2, True), ("f16", 4, 4, False), ("bf16", 4, 4, True)])
+def test_tuned_and_generic_tilings_agree(dtype, H, H_kv, causal, monkeypatch):
+    w = workloads.custom(2, H, 700, 128, dtype, causal, 3401 + H + H_kv, name="tilings", H_kv=H_kv)
+    log("case: %s seed=%d" % (w.describe(), w.seed))
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    monkeypatch.delenv("FA2_FORCE_GENERIC", raising=False)
+    tuned = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
+    monkeypatch.setenv("FA2_FORCE_GENERIC", "1")
+    generic = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
+    monkeypatch.delenv("FA2_FORCE_GENERIC")
+    tol = TOL[dtype]
+    for outs in (tuned, generic):
+        errs = check_against_oracle(w, q, k, v, dO, outs)
+        log("  errors: " + " ".join("%s=%.3g" % kv for kv in errs.items()))
+        assert all(e <= tol for e in errs.values()), errs
+    same = []
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), tuned, generic):
+        e = rel_err(a.float().cpu(), b.float().cpu())
+        same.append("%s %s" % (name, "same bits" if torch.equal(a, b) else "differs by %.3g" % e))
+        assert e <= tol, "%s: tuned and generic tilings differ by %.3g" % (name, e)
+    log("  tuned vs generic: " + ", ".join(same))
+
+
+def test_decode_split_and_unsplit_agree(monkeypatch):
+    """Decoding: the split-cache kernel against the unsplit generic path."""
+    w = workloads.DecodeWorkload("tilings_decode", 2, 16, 4, 3, 3000, 128, "bf16", True, 3402)
+    q, k, v = workloads.make_decode_inputs(w, device="cuda")
+    monkeypatch.delenv("FA2_FORCE_GENERIC", raising=False)
+    a = fa.decode(q, k, v, True, w.scale)
+    monkeypatch.setenv("FA2_FORCE_GENERIC", "1")
+    b = fa.decode(q, k, v, True, w.scale)
+    monkeypatch.delenv("FA2_FORCE_GENERIC")
+    torch.cuda.synchronize()
+    assert rel_err(a[0].float().cpu(), b[0].float().cpu()) <= TOL["bf16"]
+    assert rel_err(a[1].cpu(), b[1].cpu()) <= TOL["bf16"]

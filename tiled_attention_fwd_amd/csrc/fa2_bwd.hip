@@ -1038,7 +1038,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2 && D == 128) {
-    if (stage == 2) {
+    // (The generic dK/dV kernel walks whole groups itself, so a forced
+    // generic run never splits them and the partial sum does not run.)
+    if (stage == 2 && !force_generic_kernels()) {
       const long long blocks = (long long)((a.N + d128::BC - 1) / d128::BC) * BHkv;
       if (blocks * a.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
       const int S = a.splits;
@@ -1057,7 +1059,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       }
       return hipGetLastError();
     }
-    if (stage == 3) {
+    if (stage == 3 && !force_generic_kernels()) {
       const int num_qt = (a.N + 127) / 128;
       const long long blocks = (long long)num_qt * BH;
       if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

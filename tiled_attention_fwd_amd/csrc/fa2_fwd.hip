@@ -471,16 +471,18 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   if constexpr (sizeof(T) == 2 && D == 128) {
-    if (a.Nk > 0) return hipErrorInvalidValue;  // decoding has its own kernel here
-    const int BH = a.B * a.H;
-    const int num_qt = (a.N + fpp::BR - 1) / fpp::BR;
-    const long long blocks = (long long)num_qt * BH;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_pp_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, a.scale * kLog2e, a.H, a.H / a.Hkv, a.cu,
-                       a.T);
-    return hipGetLastError();
+    // (Decoding through this launcher, Nk > 0, takes the generic kernel.)
+    if (a.Nk == 0 && !force_generic_kernels()) {
+      const int BH = a.B * a.H;
+      const int num_qt = (a.N + fpp::BR - 1) / fpp::BR;
+      const long long blocks = (long long)num_qt * BH;
+      if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((fwd_pp_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, a.scale * kLog2e, a.H, a.H / a.Hkv, a.cu,
+                         a.T);
+      return hipGetLastError();
+    }
   }
   using C = FwdTile<T, D>;
   const int BH = a.B * a.H;

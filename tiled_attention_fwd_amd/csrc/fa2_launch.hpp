@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 namespace fa2 {
 
@@ -134,6 +135,16 @@ inline size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
   if (p.splits <= 1) return 0;
   const size_t rows = (size_t)B * H * Nq;
   return align256((size_t)p.splits * rows * d * sizeof(float)) + align256((size_t)p.splits * rows * sizeof(float));
+}
+
+// FA2_FORCE_GENERIC set to anything but "0" in the environment makes every
+// call take the generic kernels (register-staged tiles) instead of the tuned
+// 16-bit d = 128 ones, and decoding the unsplit path: a second, independent
+// tiling of the same arithmetic, for checking the two against each other.
+// Read on the host at every call; no state is kept.
+inline bool force_generic_kernels() {
+  const char* e = getenv("FA2_FORCE_GENERIC");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
 }
 
 hipError_t launch_forward(const FwdArgs& a);

@@ -33,7 +33,10 @@ def rel_err(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     denom = float(np.max(np.abs(b))) if b.size else 0.0
-    diff = float(np.max(np.abs(a - b))) if a.size else 0.0
+    with np.errstate(invalid="ignore"):  # inf - inf from a broken oracle: reported as inf below
+        diff = float(np.max(np.abs(a - b))) if a.size else 0.0
+    if not np.isfinite(diff):
+        return float("inf")
     if denom == 0.0:
         return diff
     return diff / denom

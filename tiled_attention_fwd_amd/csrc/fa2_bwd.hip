@@ -645,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
 
   const SwzOffsets so = swz_offsets(lane);
   // One step: 32 query rows against this wave's 32 keys.
-  auto step_body = [&](const T* qt, const T* gt, const float* ld, int i0, auto masked) {
+  auto step_body = [&](const T* qt, const T* gt, const float* ld, int i0, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     // Launder the lane offsets so the per-fragment XORs are recomputed each
     // step instead of being hoisted into dozens of live registers.
@@ -739,6 +739,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
     __syncthreads();
     int st = 0;
     for (; st < st_bulk_begin; ++st) step(st, BoolC<true>{});
+    if (st < st_bulk_end && (st & 1)) step(st++, BoolC<false>{});
+    // Unmasked steps in pairs with literal buffers, so the LDS read bases
+    // are immediates; the loads get the next buffer as an opaque scalar.
+    for (; st + 2 <= st_bulk_end; st += 2) {
+      int one, zero;
+      asm volatile("s_mov_b32 %0, 1" : "=s"(one));
+      asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+      issue(st + 1, one);
+      step_body(QdO[0][0], QdO[0][1], LD[0], (qt_begin + st) * BR, BoolC<false>{});
+      wait_vmem();
+      __syncthreads();
+      if (st + 2 < n_st) issue(st + 2, zero);
+      step_body(QdO[1][0], QdO[1][1], LD[1], (qt_begin + st + 1) * BR, BoolC<false>{});
+      wait_vmem();
+      __syncthreads();
+    }
     for (; st < st_bulk_end; ++st) step(st, BoolC<false>{});
     for (; st < n_st; ++st) step(st, BoolC<true>{});
   }

@@ -78,6 +78,8 @@ DECODE_CASES = [
     (1, 8, 8, 16, 16, True),
     # many chunks (32 x 128 keys)
     (2, 6, 3, 5, 4096, False),
+    # plain multi-head (one query head per cache head), split
+    (4, 8, 8, 1, 3000, True),
 ]
 
 

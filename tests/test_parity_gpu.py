@@ -287,6 +287,13 @@ def test_gqa(H, H_kv, d, causal, dtype):
     run_case(workloads.custom(2, H, 333, d, dtype, causal, seed, name="gqa", H_kv=H_kv))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [16, 32])
+def test_gqa_small_head_dims(d, dtype):
+    """Grouped heads through the generic kernels at the small head sizes."""
+    run_case(workloads.custom(2, 6, 257, d, dtype, True, 3500 + d, name="gqa", H_kv=2))
+
+
 def test_mqa_long_bf16():
     """Multi-query attention at the large workload's head size and a long,
     ragged sequence: 8 query heads on one K, V head."""

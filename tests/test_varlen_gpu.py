@@ -76,6 +76,9 @@ VARLEN_CASES = [
     ([700, 1, 257], 4, 1, 128, "f16", False),
     ([5, 130, 0, 0, 999], 3, 3, 16, "f32", True),
     ([2049, 64, 640], 2, 2, 128, "bf16", False),
+    # grouped heads in fp32 at d = 128 (generic kernels), and fp16 at d = 64
+    ([300, 1, 129, 77], 4, 2, 128, "f32", True),
+    ([513, 31], 6, 3, 64, "f16", True),
 ]
 
 

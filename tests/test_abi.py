@@ -1,7 +1,6 @@
 """The C ABI of libfa2.so on the CPU: it loads, exports every declared entry
 point, and rejects bad arguments with the documented status codes before any
 HIP call (so no GPU is needed).  Nothing here launches a kernel."""
-import ctypes
 import os
 import re
 

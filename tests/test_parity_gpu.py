@@ -15,7 +15,6 @@ kernels fail to write shows up as NaN), and sits inside a larger allocation
 whose guard bands are checked afterwards (an out-of-bounds write at a ragged
 tail changes them).
 """
-import math
 import sys
 
 import numpy as np

@@ -248,6 +248,10 @@ __device__ __forceinline__ void write_transposed4<_Float16>(_Float16* tile, int 
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Grouped-query attention: query head h of sequence b reads key/value head
+// h / G (G = H / H_kv query heads per key/value head); the kernels pass that
+// head with heads = H_kv to seq_rows below.
+//
 // Where the rows of one (sequence, head) live.  Fixed-length batches
 // ([B, heads, N, d], cu == nullptr): head (b, h) starts at row
 // (b*heads + h)*N and has N rows.  Packed ragged batches ([heads, T, d] with
@@ -273,10 +277,6 @@ __device__ __forceinline__ SeqRows seq_rows(const int* cu, int Nmax, int T, int 
   return r;
 }
 
-// Grouped-query attention: query head bh = b*H + h reads key/value head
-// (b, h / G) of the [B, H/G, N, d] key/value tensors (G = 1: plain
-// multi-head attention).  Returns that head's index b*(H/G) + h/G.
-__device__ __forceinline__ int kv_head(int bh, int H, int G) { return (bh / H) * (H / G) + (bh % H) / G; }
 
 // The value held by lane l ^ 32 (the other half of the wave), through the
 // gfx950 half-swap of two registers: a VALU operation, where a shuffle would

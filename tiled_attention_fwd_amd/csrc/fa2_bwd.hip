@@ -812,6 +812,281 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
   }
 }
 
+// dK, dV for the 16-bit types at d = 64: the d = 128 kernel's pass with
+// 128-byte LDS rows (chunk c of row r at c ^ swz64(r)), 8-row direct loads
+// and half the accumulators.
+namespace d64 {
+constexpr int D = 64;
+constexpr int ROWE = 64;   // elements per LDS row
+constexpr int BC = 128;    // keys per workgroup
+constexpr int BR = 32;     // query rows per step
+constexpr int TILE_E = BR * ROWE;
+using namespace fa2::tiles;
+}  // namespace d64
+
+// Three waves per SIMD without the mask (168 registers); the causal
+// variant keeps two, where three would spill.
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256, CAUSAL ? 2 : 3) void bwd_dkdv_d64_kernel(const T* __restrict__ Q,
+                                                               const T* __restrict__ K,
+                                                               const T* __restrict__ V,
+                                                               const T* __restrict__ dO,
+                                                               const float* __restrict__ Lse2,
+                                                               const float* __restrict__ Delta,
+                                                               T* __restrict__ dK, T* __restrict__ dV,
+                                                               int Nmax, int BHkv, float sl2, float scale, int H,
+                                                               int G, int S, float* __restrict__ PartK,
+                                                               float* __restrict__ PartV, const int* __restrict__ cu,
+                                                               int Ttot, long long kv_rows) {
+  using namespace d64;
+  constexpr int CH = 8, DCH = D / 16, NB = D / 32;
+  __shared__ __attribute__((aligned(16))) T Vs[BC * ROWE];         // 16 KB
+  __shared__ __attribute__((aligned(16))) T QdO[2][2][TILE_E];     // [buf][Q|dO], 16 KB
+  __shared__ __attribute__((aligned(16))) float LD[2][64];         // [buf][LSE2 32 | D 32]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int lin = blockIdx.x;
+  const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
+  const int sp = (lin % (BHkv * S)) / BHkv;  // which 1/S of the group's query heads
+  const int bhk = lin % BHkv;  // (sequence, key/value head)
+  const int gpw = G / S;       // query heads walked by this workgroup: h0 .. h0 + gpw - 1
+  const int bq = bhk / (H / G), hk = bhk % (H / G);
+  const int h0 = hk * G + sp * gpw;
+  const SeqRows skv = seq_rows(cu, Nmax, Ttot, bq, hk, H / G);
+  const int N = skv.n;  // this sequence's length
+  const size_t base = (size_t)skv.row0 * D;
+  if (kt * BC >= N) return;  // a tile past a shorter packed sequence
+  const T* Vh = V + base;
+  const int kv0 = kt * BC;
+  const int kw = kv0 + 32 * w;  // first key of this wave
+  const int kj = kw + l32;      // key owned by this lane
+  // Query-side sources of the query head being walked (set per head below):
+  // Q and dO as buffers, LSE * log2(e) and D.
+  u32x4 rq, rdo;
+  const float* lseh = Lse2;
+  const float* dlh = Delta;
+
+  u32x4 kf[DCH];
+  {
+    const T* krow = K + base + (size_t)min(kj, N - 1) * D + h * CH;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) kf[c] = load16(krow + c * 2 * CH);
+  }
+  f32x16 dk[NB], dv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    dk[b] = f32x16{};
+    dv[b] = f32x16{};
+  }
+
+  const int n_qt = (N + BR - 1) / BR;
+  const int qt_begin = CAUSAL ? kv0 / BR : 0;
+  const int n_st = n_qt - qt_begin;  // >= 1
+
+  // V tile: 16 one-kilobyte loads of 8 rows, 4 per wave (rows past N read
+  // row N-1).
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = 4 * w + u;
+    const int r = 8 * k + (lane >> 3);
+    const int c = (lane & 7) ^ swz64(r);
+    dload16(Vh + (size_t)min(kv0 + r, N - 1) * D + c * 8, &Vs[k * 512]);
+  }
+  // Q, dO, LSE2, D of step st into buffer buf: 2 tensors x 4 loads of 8
+  // rows, 2 per wave (waves 0-1 Q, 2-3 dO); wave 0 fetches LSE2 and D.
+  // Complete steps take the row offset as the uniform buffer offset; a
+  // ragged last step clamps its rows to N-1 per lane.
+  auto issue = [&](int st, int buf) {
+    const int step = qt_begin + st;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = 2 * w + u;
+      const int tens = q >> 2, k = q & 3;
+      const int r = 8 * k + (lane >> 3);
+      const int col = ((lane & 7) ^ swz64(r)) * 16;
+      const u32x4 rs = tens ? rdo : rq;
+      if ((step + 1) * BR <= N)
+        bload16(rs, r * 128 + col, step * BR * 128, &QdO[buf][tens][k * 512]);
+      else
+        bload16(rs, min(step * BR + r, N - 1) * 128 + col, 0, &QdO[buf][tens][k * 512]);
+    }
+    if (w == 0) {
+      const int i = min(step * BR + l32, N - 1);
+      dload4(h ? dlh + i : lseh + i, &LD[buf][0]);
+    }
+  };
+
+  const SwzOffsets so = swz_offsets64(lane);
+  // One step: 32 query rows against this wave's 32 keys.
+  auto step_body = [&](const T* qt, const T* gt, const float* ld, int i0, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // Launder the lane offsets so the per-fragment XORs are recomputed each
+    // step instead of being hoisted into dozens of live registers.
+    int rofs = so.rofs, tofs0 = so.tofs0, tofs1 = so.tofs1, kk = so.kk;
+    asm volatile("" : "+v"(rofs), "+v"(tofs0), "+v"(tofs1), "+v"(kk));
+    const char* vrow = reinterpret_cast<const char*>(Vs) + w * 32 * 128;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      const int ro = rofs ^ (c << 5);
+      mfma_chunk<T>(s, lds16(qt, ro), kf[c]);
+      mfma_chunk<T>(dp, lds16(gt, ro), lds16(vrow, ro));
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int c = 0; c < DCH - 2; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int t_causal = kj - i0 - 4 * h;  // masked when t_causal > c_r
+    const int t_rows = N - i0 - 4 * h;     // masked when c_r >= t_rows
+    const bool key_dead = kj >= N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int il = 8 * g + 4 * h;  // rows il..il+3 of this lane
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ld + il);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ld + 32 + il);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * g + q;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[q]));
+        if (MASKED) {
+          const int c_r = 8 * g + q;
+          p = ((CAUSAL & (t_causal > c_r)) | (c_r >= t_rows) | key_dead) ? 0.f : p;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[q]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pb = pack_chunk<T>(s, t);
+      const u32x4 sb = pack_chunk<T>(dp, t);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int cb = ((b ^ kk) << 6) + t * 2048;
+        mfma_chunk<T>(dv[b], tr_frag(gt, tofs0 + cb, tofs1 + cb), pb);
+        mfma_chunk<T>(dk[b], tr_frag(qt, tofs0 + cb, tofs1 + cb), sb);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto step = [&](int st, auto masked) {
+    const int buf = st & 1;
+    if (st + 1 < n_st) issue(st + 1, buf ^ 1);
+    const int i0 = (qt_begin + st) * BR;
+    // Skip blocks with no visible key (all above the diagonal, or keys past
+    // N); they would only add zeros.
+    if (!decltype(masked)::value || (kw < N && (!CAUSAL || i0 + 31 >= kw)))
+      step_body(QdO[buf][0], QdO[buf][1], LD[buf], i0, masked);
+    wait_vmem();
+    __syncthreads();
+  };
+  // Steps off the diagonal band, complete (32 rows < N) and on a complete key
+  // tile need no mask; only a prefix (the diagonal) and the ragged end do.
+  const int full_steps = N / BR - qt_begin;
+  const int st_bulk_begin = (kv0 + BC > N) ? n_st : (CAUSAL ? min(n_st, BC / BR) : 0);
+  const int st_bulk_end = max(st_bulk_begin, min(n_st, full_steps));
+  // The walk is repeated for each query head that shares these keys
+  // (grouped-query attention), accumulating into the same dK, dV.
+  for (int g = 0; g < gpw; ++g) {
+    const long long qrow0 = seq_rows(cu, Nmax, Ttot, bq, h0 + g, H).row0;
+    rq = make_rsrc(Q + (size_t)qrow0 * D, (unsigned)N * D * 2);
+    rdo = make_rsrc(dO + (size_t)qrow0 * D, (unsigned)N * D * 2);
+    lseh = Lse2 + qrow0;
+    dlh = Delta + qrow0;
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    int st = 0;
+    for (; st < st_bulk_begin; ++st) step(st, BoolC<true>{});
+    if (st < st_bulk_end && (st & 1)) step(st++, BoolC<false>{});
+    // Unmasked steps in pairs with literal buffers, so the LDS read bases
+    // are immediates; the loads get the next buffer as an opaque scalar.
+    for (; st + 2 <= st_bulk_end; st += 2) {
+      int one, zero;
+      asm volatile("s_mov_b32 %0, 1" : "=s"(one));
+      asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+      issue(st + 1, one);
+      step_body(QdO[0][0], QdO[0][1], LD[0], (qt_begin + st) * BR, BoolC<false>{});
+      wait_vmem();
+      __syncthreads();
+      if (st + 2 < n_st) issue(st + 2, zero);
+      step_body(QdO[1][0], QdO[1][1], LD[1], (qt_begin + st + 1) * BR, BoolC<false>{});
+      wait_vmem();
+      __syncthreads();
+    }
+    for (; st < st_bulk_end; ++st) step(st, BoolC<false>{});
+    for (; st < n_st; ++st) step(st, BoolC<true>{});
+  }
+
+  if (S > 1) {
+    // One of S partial sums over the group: fp32 rows of [S][kv_rows, d]
+    // (kv_rows = the rows of dK), dK already scaled; bwd_dkdv_reduce_kernel
+    // adds them up.
+    if (kj < N) {
+      const size_t row = (size_t)sp * kv_rows + skv.row0 + kj;
+      float* pk = PartK + row * D;
+      float* pv = PartV + row * D;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * b + 8 * g + 4 * h;
+          *reinterpret_cast<f32x4*>(pk + d0) = f32x4{dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale,
+                                                      dk[b][4 * g + 2] * scale, dk[b][4 * g + 3] * scale};
+          *reinterpret_cast<f32x4*>(pv + d0) = f32x4{dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2],
+                                                      dv[b][4 * g + 3]};
+        }
+      }
+    }
+    return;
+  }
+  // Stage the bf16 results row-major in LDS (16-byte chunks swizzled like
+  // the tiles): dK in the V tile, dV in the Q/dO buffers, both free now.
+  T* sk = Vs;
+  T* sv = &QdO[0][0][0];
+  {
+    const int row = 32 * w + l32;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = row * ROWE + (((4 * b + g) ^ swz64(row)) << 3) + 4 * h;
+        store4<T>(sk + off, dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale, dk[b][4 * g + 2] * scale,
+                  dk[b][4 * g + 3] * scale);
+        store4<T>(sv + off, dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2], dv[b][4 * g + 3]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * w + 8 * i + (lane >> 3);
+    const int ch = lane & 7;
+    const int key = kv0 + row;
+    if (key < N) {
+      const int off = (row * ROWE + ((ch ^ swz64(row)) << 3)) * 2;
+      store16(dK + base + (size_t)key * D + ch * 8, lds16(sk, off));
+      store16(dV + base + (size_t)key * D + ch * 8, lds16(sv, off));
+    }
+  }
+}
+
 // dQ for the 16-bit types at d = 128: the pass of bwd_dq_kernel organised like the
 // d = 128 forward.  32-key blocks of K and V reach LDS through direct loads
 // into a ring of 4 slots (unpadded swizzled rows), issued 3 blocks ahead,
@@ -1083,6 +1358,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                          static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse2, a.delta,
                          static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (sizeof(T) == 2 && D == 64) {
+    if (stage == 2 && !force_generic_kernels()) {
+      const long long blocks = (long long)((a.N + d64::BC - 1) / d64::BC) * BHkv;
+      if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((bwd_dkdv_d64_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         static_cast<const T*>(a.dO), a.lse2, a.delta, static_cast<T*>(a.dk),
+                         static_cast<T*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G, 1, a.part, a.part, a.cu, a.T,
+                         kv_rows);
       return hipGetLastError();
     }
   }

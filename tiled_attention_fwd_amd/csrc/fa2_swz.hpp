@@ -89,6 +89,28 @@ __device__ __forceinline__ SwzOffsets swz_offsets(int lane) {
   o.kk = s0 >> 2;
   return o;
 }
+// 128-byte rows (d = 64): chunk c (0..7) of row r is stored at c ^ swz64(r).
+// Over 16 consecutive rows the 8 even rows take 8 distinct values, and so do
+// the 8 odd ones, so 16 lanes reading one chunk of 16 rows hit every bank
+// once; bit 2 is (r >> 1) & 1, so rows r and r + 2 of a transposed read's
+// 4-row group sit in different 64-byte halves and its 32 lanes also cover
+// every bank once.
+__device__ __forceinline__ int swz64(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+// Lane offsets for 128-byte rows, as swz_offsets: row fragment (chunk
+// 2c + h of row l32) at rofs ^ (c << 5); transpose fragment (t, column
+// block b) at t*2048 + tofs{0,1} + ((b ^ kk) << 6).
+__device__ __forceinline__ SwzOffsets swz_offsets64(int lane) {
+  const int l32 = lane & 31, h = lane >> 5, j = lane & 15;
+  SwzOffsets o;
+  o.rofs = l32 * 128 + ((h ^ swz64(l32)) << 4);
+  const int r0 = 4 * h + (j >> 2);  // < 8: swz64(r0 + 8) = swz64(r0) ^ 2
+  const int f0 = (r0 >> 2) & 3;
+  const int c1 = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+  o.tofs0 = r0 * 128 + ((c1 ^ f0) << 4) + 8 * (j & 1);
+  o.tofs1 = (r0 + 8) * 128 + ((c1 ^ (f0 ^ 2)) << 4) + 8 * (j & 1);
+  o.kk = (r0 >> 1) & 1;
+  return o;
+}
 __device__ __forceinline__ u32x4 lds16(const void* base, int byte_off) {
   return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
 }

@@ -25,7 +25,8 @@
 //                    read from the row-major LDS tiles by transpose reads.
 //                    For bf16 and fp16 at d = 128, bwd_dkdv_d128_kernel
 //                    runs the same pass with direct-to-LDS loads into
-//                    swizzled tiles and two independent workgroups per CU.
+//                    swizzled tiles and two independent workgroups per CU;
+//                    bwd_dkdv_d64_kernel does the same at d = 64.
 //                    With grouped-query heads a workgroup walks every query
 //                    head of its key/value head's group (or a 1/S share of
 //                    them, bwd_dkdv_reduce_kernel then summing the S fp32

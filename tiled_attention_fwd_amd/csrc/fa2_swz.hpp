@@ -1,7 +1,8 @@
 // fa2_swz.hpp -- swizzled LDS tiles and direct global-to-LDS loads (gfx950).
 //
-// Shared by the forward, backward and decode kernels for the 16-bit types at d = 128, whose
-// tiles are stored unpadded, 256 bytes per row, and filled by direct loads
+// Shared by the forward, backward and decode kernels for the 16-bit types at
+// d = 128, whose tiles are stored unpadded, 256 bytes per row, and by the
+// d = 64 dK/dV kernel (128-byte rows, swz64); all are filled by direct loads
 // (no register staging).
 #pragma once
 #include "fa2_common.hpp"

@@ -327,13 +327,18 @@ def test_gqa_backward_bitwise_repeatable():
         assert torch.equal(x, y)
 
 
-# Two independent tilings of the 16-bit d = 128 path: the tuned kernels
-# (direct loads into swizzled LDS rings) and the generic ones (register-staged
-# padded tiles), selected by FA2_FORCE_GENERIC.  Both must meet the tolerance
-# against the oracle and agree with each other within it.
-@pytest.mark.parametrize("dtype,H,H_kv,causal", [("bf16", 8, 2, True), ("f16", 4, 4, False), ("bf16", 4, 4, True)])
-def test_tuned_and_generic_tilings_agree(dtype, H, H_kv, causal, monkeypatch):
-    w = workloads.custom(2, H, 700, 128, dtype, causal, 3401 + H + H_kv, name="tilings", H_kv=H_kv)
+# Two independent tilings of the 16-bit d = 128 and d = 64 paths: the tuned
+# kernels (direct loads into swizzled LDS rings) and the generic ones
+# (register-staged padded tiles), selected by FA2_FORCE_GENERIC.  Both must
+# meet the tolerance against the oracle and agree with each other within it;
+# the forward passes walk the same 32-key blocks with the same rescale rule
+# and product order, so O and LSE must come out bit-identical.
+@pytest.mark.parametrize("dtype,H,H_kv,causal,d,qk_mult", [
+    ("bf16", 8, 2, True, 128, 1.0), ("f16", 4, 4, False, 128, 1.0), ("bf16", 4, 4, True, 128, 1.0),
+    ("bf16", 4, 4, False, 64, 8.0), ("f16", 8, 2, True, 64, 1.0), ("bf16", 4, 4, True, 64, 1.0)])
+def test_tuned_and_generic_tilings_agree(dtype, H, H_kv, causal, d, qk_mult, monkeypatch):
+    w = workloads.custom(2, H, 700, d, dtype, causal, 3401 + H + H_kv + d, name="tilings", H_kv=H_kv,
+                         qk_mult=qk_mult)
     log("case: %s seed=%d" % (w.describe(), w.seed))
     q, k, v, dO = workloads.make_inputs(w, device="cuda")
     monkeypatch.delenv("FA2_FORCE_GENERIC", raising=False)
@@ -352,6 +357,7 @@ def test_tuned_and_generic_tilings_agree(dtype, H, H_kv, causal, monkeypatch):
         same.append("%s %s" % (name, "same bits" if torch.equal(a, b) else "differs by %.3g" % e))
         assert e <= tol, "%s: tuned and generic tilings differ by %.3g" % (name, e)
     log("  tuned vs generic: " + ", ".join(same))
+    assert torch.equal(tuned[0], generic[0]) and torch.equal(tuned[1], generic[1])
 
 
 def test_decode_split_and_unsplit_agree(monkeypatch):

@@ -247,10 +247,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   }
 }
 
-// Forward for the 16-bit types at d = 128.  Same pass as fwd_kernel, organised around
-// 32-key blocks that reach LDS through direct loads into a ring of 4 block
-// slots (K and V, unpadded swizzled rows), issued 3 blocks ahead, one
-// barrier per block.  Within a wave the score products of block b+1 are
+// Forward for the 16-bit types at d = 128 and d = 64.  Same pass as
+// fwd_kernel, organised around 32-key blocks that reach LDS through direct
+// loads into a ring of 4 block slots (K and V, unpadded swizzled rows:
+// 256-byte rows swizzled by swz, 128-byte rows by swz64), issued 3 blocks
+// ahead, one barrier per block.  Within a wave the score products of block b+1 are
 // issued before the softmax of block b, so the matrix cores have work while
 // the exponentials of block b run; then P V of block b follows.
 //
@@ -264,22 +265,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
 // the uniform buffer offset, and the rare running-max rescale is a real
 // branch.
 namespace fpp {
-constexpr int D = 128;
-constexpr int ROWE = 128;
 constexpr int BR = 128;        // query rows per workgroup (4 waves x 32)
 constexpr int KB = 32;         // keys per block
-constexpr int BLK_E = KB * ROWE;
+// Workgroups per CU: at d = 64 three fit (168 registers, 3 x 32 KB of LDS).
+constexpr int occupancy(int D) { return D == 64 ? 3 : 2; }
 }  // namespace fpp
 
-template <typename T, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, fpp::occupancy(D)) void fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, T* __restrict__ O,
                                                         float* __restrict__ LSE, int Nmax, int BH, int num_qt,
                                                         float sl2, int H, int G, const int* __restrict__ cu,
                                                         int Ttot) {
   using namespace tiles;
-  constexpr int D = fpp::D, KB = fpp::KB, BLK_E = fpp::BLK_E;
+  static_assert(D == 128 || D == 64, "fwd_pp_kernel: d = 128 or 64");
+  constexpr int KB = fpp::KB, BLK_E = KB * D;
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
+  constexpr int ROWB = 2 * D;           // bytes per LDS row
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;      // rows per 1-KB wave load
+  constexpr int LPT = KB / RPL;         // loads per tensor per block
+  constexpr int LPW = 2 * LPT / 4;      // loads per wave per block
   constexpr int R = 4, PF = R - 1;  // ring slots, blocks loaded ahead
   __shared__ __attribute__((aligned(16))) T Ks[R][BLK_E];
   __shared__ __attribute__((aligned(16))) T Vs[R][BLK_E];
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
   // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
-  // q = 4w + u, rows 4(q%8)..+3 of the block.
+  // q = LPW w + u, rows RPL (q % LPT) .. + RPL - 1 of the block.
   const long long kv_row0 = seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0;
   const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_row0 * D, (unsigned)N * D * 2);
   T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
@@ -310,13 +316,14 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
   // Per-lane constants: direct-load offsets within a block, and the LDS
   // fragment offsets (K row fragments by chunk, V transpose fragments by
   // column block and half); block slots and the t half are immediates.
-  int voff[4];
+  auto swz_row = [](int r) { return D == 128 ? swz(r) : swz64(r); };
+  int voff[LPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
-    voff[u] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+  for (int u = 0; u < LPW; ++u) {
+    const int r = RPL * ((LPW * w + u) % LPT) + lane / CPR;
+    voff[u] = r * ROWB + (((lane % CPR) ^ swz_row(r)) << 4);
   }
-  const SwzOffsets so = swz_offsets(lane);
+  const SwzOffsets so = D == 128 ? swz_offsets(lane) : swz_offsets64(lane);
   int kofs[DCH], vofs0[NB], vofs1[NB];
 #pragma unroll
   for (int c = 0; c < DCH; ++c) kofs[c] = so.rofs ^ (c << 5);
@@ -332,12 +339,13 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
     T* dst = dst0 + slot * BLK_E;
     if (row0 + KB <= N) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) bload16(rsrc, voff[u], row0 * 256, dst + ((4 * w + u) & 7) * 512);
+      for (int u = 0; u < LPW; ++u) bload16(rsrc, voff[u], row0 * ROWB, dst + ((LPW * w + u) % LPT) * 512);
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
-        bload16(rsrc, min(row0 + r, N - 1) * 256 + (voff[u] & 255), 0, dst + ((4 * w + u) & 7) * 512);
+      for (int u = 0; u < LPW; ++u) {
+        const int r = RPL * ((LPW * w + u) % LPT) + lane / CPR;
+        bload16(rsrc, min(row0 + r, N - 1) * ROWB + (voff[u] & (ROWB - 1)), 0,
+                dst + ((LPW * w + u) % LPT) * 512);
       }
     }
   };
@@ -418,12 +426,13 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
     for (int t = 0; t < 2; ++t) {
       const u32x4 pb = pack_chunk<T>(s, t);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) mfma_chunk<T>(o[b], tr_frag(vb_, vofs0[b] + t * 4096, vofs1[b] + t * 4096), pb);
+      for (int b = 0; b < NB; ++b)
+        mfma_chunk<T>(o[b], tr_frag(vb_, vofs0[b] + t * 16 * ROWB, vofs1[b] + t * 16 * ROWB), pb);
     }
-    // Blocks kb+1 .. kb+PF-1 must be in LDS for the next block; the loads of
-    // block kb+PF issued above may stay in flight.
+    // Blocks kb+1 .. kb+PF-1 must be in LDS for the next block; the LPW
+    // loads of block kb+PF issued above may stay in flight.
     if (ahead)
-      wait_vmem4();
+      wait_vmem_n<LPW>();
     else
       wait_vmem();
     __syncthreads();
@@ -470,14 +479,14 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(const T* __restrict__ Q,
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  if constexpr (sizeof(T) == 2 && D == 128) {
+  if constexpr (sizeof(T) == 2 && (D == 128 || D == 64)) {
     // (Decoding through this launcher, Nk > 0, takes the generic kernel.)
     if (a.Nk == 0 && !force_generic_kernels()) {
       const int BH = a.B * a.H;
       const int num_qt = (a.N + fpp::BR - 1) / fpp::BR;
       const long long blocks = (long long)num_qt * BH;
       if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((fwd_pp_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+      hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                          static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, a.scale * kLog2e, a.H, a.H / a.Hkv, a.cu,
                          a.T);

@@ -68,6 +68,12 @@ __device__ __forceinline__ void bload16(u32x4 r, int voffset, int soffset, const
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(4): all but the last four vector memory operations done.
 __device__ __forceinline__ void wait_vmem4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
+// s_waitcnt vmcnt(n): all but the last n vector memory operations done.
+template <int n>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(n >= 0 && n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+}
 
 // Byte offsets inside a swizzled tile.  The swizzle only touches bits 4..7
 // of a row's byte offset, so every fragment offset a lane needs is one of a

@@ -1098,8 +1098,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
                                                               const T* __restrict__ K,
                                                               const T* __restrict__ V,
                                                               const T* __restrict__ dO,
-                                                              const float* __restrict__ Lse2,
-                                                              const float* __restrict__ Delta,
+                                                              const T* __restrict__ O,
+                                                              const float* __restrict__ LSE,
+                                                              float* __restrict__ Lse2,
+                                                              float* __restrict__ Delta,
                                                               T* __restrict__ dQ, int Nmax, int BH, int num_qt,
                                                               float sl2, float scale, int H, int G,
                                                               const int* __restrict__ cu, int Ttot) {
@@ -1165,10 +1167,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
     }
   };
 
-  // Q and dO rows of this lane (B operands), its LSE (base 2) and D.  Rows
-  // past N read row N-1 and are never stored.
+  // Q and dO rows of this lane (B operands), its LSE (base 2) and D, which
+  // this kernel computes for its own rows and writes to the workspace for
+  // the dK/dV kernel that runs after it.  Rows past N read row N-1 and are
+  // never stored.
   const int qc = min(qi, N - 1);
   u32x4 qf[DCH], gf[DCH];
+  float pc[DCH];
   {
     const size_t off = base + (size_t)qc * D + h * CH;
 #pragma unroll
@@ -1176,9 +1181,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
       qf[c] = load16(Q + off + c * 2 * CH);
       gf[c] = load16(dO + off + c * 2 * CH);
     }
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) pc[c] = dot_chunk<T>(load16(O + off + c * 2 * CH), gf[c]);
   }
-  const float lse2 = Lse2[sq.row0 + qc];
-  const float dl = Delta[sq.row0 + qc];
+  // D = rowsum(dO * O).  Fragment c of this lane is 16-byte chunk 2c + h of
+  // the row; the sums pair chunks as the row-parallel bwd_pre_kernel's
+  // butterfly does (offsets 8, 4, 2, 1 over the 16 chunks), so both give the
+  // same bits.
+  const float dh = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
+  const float dl = dh + swap_halves(dh, lane);
+  const float lse2 = LSE[sq.row0 + qc] * kLog2e;
+  if (h == 0 && qi < N) {
+    Delta[sq.row0 + qi] = dl;
+    Lse2[sq.row0 + qi] = lse2;
+  }
 #pragma unroll
   for (int b = 0; b < PF; ++b)
     if (b < nb) issue(b, b);
@@ -1323,6 +1339,21 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const long long kv_rows = a.cu ? (long long)a.Hkv * a.T : (long long)BHkv * a.N;
   const float sl2 = a.scale * kLog2e;
   if (stage == 1) {
+    if constexpr (sizeof(T) == 2 && D == 128) {
+      // The dQ kernel computes D and LSE * log2(e) for its own rows, so for
+      // these types it is stage 1 and stage 3 has nothing left to do.
+      if (!force_generic_kernels()) {
+        const int num_qt = (a.N + 127) / 128;
+        const long long blocks = (long long)num_qt * BH;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_dq_d128_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), static_cast<const T*>(a.dO),
+                           static_cast<const T*>(a.o), a.lse, a.lse2, a.delta, static_cast<T*>(a.dq), a.N, BH,
+                           num_qt, sl2, a.scale, a.H, G, a.cu, a.T);
+        return hipGetLastError();
+      }
+    }
     constexpr int RPB = 256 / (D / Elt<T>::CH);
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.lse, a.delta, a.lse2,
@@ -1351,16 +1382,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       }
       return hipGetLastError();
     }
-    if (stage == 3 && !force_generic_kernels()) {
-      const int num_qt = (a.N + 127) / 128;
-      const long long blocks = (long long)num_qt * BH;
-      if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((bwd_dq_d128_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                         static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                         static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse2, a.delta,
-                         static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T);
-      return hipGetLastError();
-    }
+    if (stage == 3 && !force_generic_kernels()) return hipSuccess;  // dQ came with stage 1
   }
   if constexpr (sizeof(T) == 2 && D == 64) {
     if (stage == 2 && !force_generic_kernels()) {

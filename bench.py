@@ -4,8 +4,8 @@
 One step = the whole hot path over one batch of the large causal bf16
 workload (B=4, H=16, N=4096, d=128): ``fa2_forward`` and then the three
 backward stages (D = rowsum(dO * O), the dK/dV kernel, the dQ kernel; at
-d = 128 in the 16-bit types the dQ kernel computes D itself and runs as
-stage 1, and stage 3 is empty), i.e. exactly ``fa2_backward``, called stage
+d = 128 and 64 in the 16-bit types the dQ kernel computes D itself and runs
+as stage 1, and stage 3 is empty), i.e. exactly ``fa2_backward``, called stage
 by stage so that HIP events on the launch stream can time each kernel.  The default 30 warmup steps let
 the clocks settle; 100 timed steps take about 0.15 s.  Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.
@@ -72,10 +72,10 @@ KERNEL_SOURCES = {
 
 def stage_kernels(dtype: str, d: int) -> list:
     """Kernel names of the forward call and backward stages 1, 2, 3, in order.
-    For the 16-bit types at d = 128 the dQ kernel computes D and LSE*log2(e)
-    itself and runs as stage 1; stage 3 then enqueues nothing."""
+    For the 16-bit types at d = 128 and 64 the dQ kernel computes D and
+    LSE*log2(e) itself and runs as stage 1; stage 3 then enqueues nothing."""
     generic = os.environ.get("FA2_FORCE_GENERIC", "") not in ("", "0")
-    if dtype in ("bf16", "f16") and d == 128 and not generic:
+    if dtype in ("bf16", "f16") and d in (128, 64) and not generic:
         return ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_stage3_empty"]
     return ["fwd_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
 

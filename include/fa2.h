@@ -108,7 +108,7 @@ int fa2_backward(const void* q, const void* k, const void* v, const void* o,
 /*
  * One stage of fa2_backward, with exactly fa2_backward's arguments and
  * checks: stage 1 = D and LSE * log2(e), 2 = the dK/dV kernel, 3 = the dQ
- * kernel.  For bf16 and fp16 at d = 128 (unless FA2_FORCE_GENERIC is set)
+ * kernel.  For bf16 and fp16 at d = 128 and 64 (unless FA2_FORCE_GENERIC is set)
  * the dQ kernel computes D and LSE * log2(e) for its own rows, so stage 1
  * is the dQ kernel (dq is written by it) and stage 3 enqueues nothing.
  * Enqueuing stages 1, 2, 3 in order on one stream is fa2_backward; the

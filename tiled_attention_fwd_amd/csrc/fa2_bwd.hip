@@ -14,7 +14,8 @@
 //
 // Kernels, in stream order:
 //   bwd_pre_kernel   D = rowsum(dO o O) in fp32 (HBM-bound, one pass over O
-//                    and dO), and LSE * log2(e) for the dK/dV kernel.
+//                    and dO), and LSE * log2(e) for the dK/dV kernel; not
+//                    run where bwd_dq_pp_kernel computes them (below).
 //   bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile); each of
 //                    its 4 waves owns 32 keys and keeps K, V (as MFMA B
 //                    operands) and its dK^T, dV^T accumulators in registers
@@ -35,8 +36,10 @@
 //                    like the forward pass: S^T = K Q^T and dP^T = V dO^T on
 //                    MFMA, so each lane owns one query and its LSE and D are
 //                    scalars, then dQ^T += K^T dS^T.  For the 16-bit types
-//                    at d = 128, bwd_dq_d128_kernel runs it over a ring of
-//                    direct-loaded 32-key blocks, like the d = 128 forward.
+//                    at d = 128 and 64, bwd_dq_pp_kernel runs it over a ring
+//                    of direct-loaded 32-key blocks, like fwd_pp_kernel, and
+//                    computes D and LSE * log2(e) for its own rows on the
+//                    way (it is then stage 1, ahead of dK/dV).
 // Every kernel takes its (sequence, head) rows from seq_rows, so fixed-length
 // and packed ragged batches share them.
 // The two halves recompute S and dP instead of exchanging dS, so dQ needs no
@@ -1088,13 +1091,18 @@ __global__ __launch_bounds__(256, CAUSAL ? 2 : 3) void bwd_dkdv_d64_kernel(const
   }
 }
 
-// dQ for the 16-bit types at d = 128: the pass of bwd_dq_kernel organised like the
-// d = 128 forward.  32-key blocks of K and V reach LDS through direct loads
-// into a ring of 4 slots (unpadded swizzled rows), issued 3 blocks ahead,
-// one barrier per block; lane offsets of every fragment and load are
-// computed once and the block loop is unrolled over the ring.
-template <typename T, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict__ Q,
+// dQ for the 16-bit types at d = 128 and d = 64: the pass of bwd_dq_kernel
+// organised like fwd_pp_kernel.  32-key blocks of K and V reach LDS through
+// direct loads into a ring of 4 slots (unpadded swizzled rows: 256-byte rows
+// swizzled by swz, 128-byte rows by swz64), issued 3 blocks ahead, one
+// barrier per block; lane offsets of every fragment and load are computed
+// once and the block loop is unrolled over the ring.
+namespace dqpp {
+// Workgroups per CU: at d = 64 three fit (3 x 32 KB of LDS).
+constexpr int occupancy(int D) { return D == 64 ? 3 : 2; }
+}  // namespace dqpp
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, dqpp::occupancy(D)) void bwd_dq_pp_kernel(const T* __restrict__ Q,
                                                               const T* __restrict__ K,
                                                               const T* __restrict__ V,
                                                               const T* __restrict__ dO,
@@ -1106,7 +1114,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
                                                               float sl2, float scale, int H, int G,
                                                               const int* __restrict__ cu, int Ttot) {
   using namespace tiles;
-  constexpr int D = 128, KB = 32, BLK_E = KB * 128, CH = 8, DCH = D / 16, NB = D / 32;
+  static_assert(D == 128 || D == 64, "bwd_dq_pp_kernel: d = 128 or 64");
+  constexpr int KB = 32, BLK_E = KB * D, CH = 8, DCH = D / 16, NB = D / 32;
+  constexpr int ROWB = 2 * D;       // bytes per LDS row
+  constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;  // rows per 1-KB wave load
+  constexpr int LPT = KB / RPL;     // loads per tensor per block
+  constexpr int LPW = 2 * LPT / 4;  // loads per wave per block
   constexpr int QB = 128;           // query rows per workgroup (4 waves x 32)
   constexpr int R = 4, PF = R - 1;  // ring slots, blocks loaded ahead
   __shared__ __attribute__((aligned(16))) T Ks[R][BLK_E];
@@ -1126,7 +1140,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
   // Waves 0-1 load K rows, waves 2-3 V rows: load u of wave w is number
-  // q = 4w + u, rows 4(q%8)..+3 of the block.
+  // q = LPW w + u, rows RPL (q % LPT) .. + RPL - 1 of the block.
   const long long kv_row0 = seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0;
   const u32x4 rsrc = make_rsrc((w < 2 ? K : V) + (size_t)kv_row0 * D, (unsigned)N * D * 2);
   T* const dst0 = w < 2 ? &Ks[0][0] : &Vs[0][0];
@@ -1136,13 +1150,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
 
   // Per-lane constants: load offsets within a block and LDS fragment offsets
   // (row fragments by chunk, transpose fragments by column block and half).
-  int voff[4];
+  auto swz_row = [](int r) { return D == 128 ? swz(r) : swz64(r); };
+  int voff[LPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
-    voff[u] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+  for (int u = 0; u < LPW; ++u) {
+    const int r = RPL * ((LPW * w + u) % LPT) + lane / CPR;
+    voff[u] = r * ROWB + (((lane % CPR) ^ swz_row(r)) << 4);
   }
-  const SwzOffsets so = swz_offsets(lane);
+  const SwzOffsets so = D == 128 ? swz_offsets(lane) : swz_offsets64(lane);
   int kofs[DCH], tofs0[NB], tofs1[NB];
 #pragma unroll
   for (int c = 0; c < DCH; ++c) kofs[c] = so.rofs ^ (c << 5);
@@ -1157,12 +1172,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
     T* dst = dst0 + slot * BLK_E;
     if (row0 + KB <= N) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) bload16(rsrc, voff[u], row0 * 256, dst + ((4 * w + u) & 7) * 512);
+      for (int u = 0; u < LPW; ++u) bload16(rsrc, voff[u], row0 * ROWB, dst + ((LPW * w + u) % LPT) * 512);
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * ((4 * w + u) & 7) + (lane >> 4);
-        bload16(rsrc, min(row0 + r, N - 1) * 256 + (voff[u] & 255), 0, dst + ((4 * w + u) & 7) * 512);
+      for (int u = 0; u < LPW; ++u) {
+        const int r = RPL * ((LPW * w + u) % LPT) + lane / CPR;
+        bload16(rsrc, min(row0 + r, N - 1) * ROWB + (voff[u] & (ROWB - 1)), 0,
+                dst + ((LPW * w + u) % LPT) * 512);
       }
     }
   };
@@ -1186,9 +1202,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
   }
   // D = rowsum(dO * O).  Fragment c of this lane is 16-byte chunk 2c + h of
   // the row; the sums pair chunks as the row-parallel bwd_pre_kernel's
-  // butterfly does (offsets 8, 4, 2, 1 over the 16 chunks), so both give the
-  // same bits.
-  const float dh = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
+  // butterfly does (offsets CPR/2 .. 1 over the row's CPR chunks), so both
+  // give the same bits.
+  float dh;
+  if constexpr (D == 128)
+    dh = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
+  else
+    dh = (pc[0] + pc[2]) + (pc[1] + pc[3]);
   const float dl = dh + swap_halves(dh, lane);
   const float lse2 = LSE[sq.row0 + qc] * kLog2e;
   if (h == 0 && qi < N) {
@@ -1216,7 +1236,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
     // LDS reads run three chunks ahead of the products that use them.
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < DCH - 3; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
@@ -1254,18 +1274,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_d128_kernel(const T* __restrict
     for (int t = 0; t < 2; ++t) {
       const u32x4 sb = pack_chunk<T>(dp, t);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) mfma_chunk<T>(dq[b], tr_frag(kb_, tofs0[b] + t * 4096, tofs1[b] + t * 4096), sb);
+      for (int b = 0; b < NB; ++b)
+        mfma_chunk<T>(dq[b], tr_frag(kb_, tofs0[b] + t * 16 * ROWB, tofs1[b] + t * 16 * ROWB), sb);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 2 * NB - 3; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (ahead)
-      wait_vmem4();
+      wait_vmem_n<LPW>();
     else
       wait_vmem();
     __syncthreads();
@@ -1339,14 +1360,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const long long kv_rows = a.cu ? (long long)a.Hkv * a.T : (long long)BHkv * a.N;
   const float sl2 = a.scale * kLog2e;
   if (stage == 1) {
-    if constexpr (sizeof(T) == 2 && D == 128) {
+    if constexpr (sizeof(T) == 2 && (D == 128 || D == 64)) {
       // The dQ kernel computes D and LSE * log2(e) for its own rows, so for
-      // these types it is stage 1 and stage 3 has nothing left to do.
+      // these types and head sizes it is stage 1 and stage 3 has nothing
+      // left to do.
       if (!force_generic_kernels()) {
         const int num_qt = (a.N + 127) / 128;
         const long long blocks = (long long)num_qt * BH;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((bwd_dq_d128_kernel<T, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((bwd_dq_pp_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), static_cast<const T*>(a.dO),
                            static_cast<const T*>(a.o), a.lse, a.lse2, a.delta, static_cast<T*>(a.dq), a.N, BH,
@@ -1360,6 +1382,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
                        rows);
     return hipGetLastError();
   }
+  if constexpr (sizeof(T) == 2 && (D == 128 || D == 64))
+    if (stage == 3 && !force_generic_kernels()) return hipSuccess;  // dQ came with stage 1
   if constexpr (sizeof(T) == 2 && D == 128) {
     // (The generic dK/dV kernel walks whole groups itself, so a forced
     // generic run never splits them and the partial sum does not run.)
@@ -1382,7 +1406,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       }
       return hipGetLastError();
     }
-    if (stage == 3 && !force_generic_kernels()) return hipSuccess;  // dQ came with stage 1
+
   }
   if constexpr (sizeof(T) == 2 && D == 64) {
     if (stage == 2 && !force_generic_kernels()) {

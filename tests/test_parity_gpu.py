@@ -372,3 +372,31 @@ def test_decode_split_and_unsplit_agree(monkeypatch):
     torch.cuda.synchronize()
     assert rel_err(a[0].float().cpu(), b[0].float().cpu()) <= TOL["bf16"]
     assert rel_err(a[1].cpu(), b[1].cpu()) <= TOL["bf16"]
+
+
+# fa2_backward_stage 1, 2, 3 in order is fa2_backward, whichever kernel each
+# stage enqueues: the dQ kernel with D as stage 1 (16-bit, d = 128 and 64),
+# the row-parallel D pass (other types and head sizes), the split grouped
+# dK/dV with its partial sum (grouped-query at d = 128).
+@pytest.mark.parametrize("dtype,H,H_kv,d,causal", [("bf16", 4, 4, 128, True), ("f16", 4, 2, 64, False),
+                                                  ("f32", 2, 2, 64, True), ("bf16", 8, 1, 128, True),
+                                                  ("bf16", 2, 2, 32, False)])
+def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
+    w = workloads.custom(2, H, 333, d, dtype, causal, 7100 + d + H_kv, name="stages", H_kv=H_kv)
+    log("case: %s seed=%d" % (w.describe(), w.seed))
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    B, _, N, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.fa2_forward_ex(q, k, v, o, lse, causal, w.scale)
+    ws = torch.empty(max(fa.fa2_backward_workspace_size_ex(B, H, H_kv, N, d, q.dtype), 16), dtype=torch.uint8,
+                     device="cuda")
+    full = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    fa.fa2_backward_ex(q, k, v, o, dO, lse, *full, causal, w.scale, ws)
+    staged = [torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))]
+    ws.fill_(0xFF)
+    for st in (1, 2, 3):
+        fa.fa2_backward_stage_ex(st, q, k, v, o, dO, lse, *staged, causal, w.scale, ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), staged, full):
+        assert torch.equal(a, b), "%s: staged backward differs from fa2_backward" % name

@@ -1406,7 +1406,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       }
       return hipGetLastError();
     }
-
   }
   if constexpr (sizeof(T) == 2 && D == 64) {
     if (stage == 2 && !force_generic_kernels()) {

@@ -215,7 +215,7 @@ int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const voi
  *   q, o   [B, H, N_q, d] (dtype); k, v [B, H_kv, N_k, d] (dtype), H_kv
  *          dividing H, query head h reading key/value head h / (H / H_kv);
  *   lse    [B, H, N_q] float, natural log, as fa2_forward.
- * Arithmetic as fa2_forward.  For FA2_BF16 and FA2_F16 with d = 128 the
+ * Arithmetic as fa2_forward.  For FA2_BF16 and FA2_F16 with d = 128 or 64 the
  * cache is split into chunks walked by separate workgroups, and a second
  * kernel merges their normalised partial outputs with weights
  * exp(LSE_chunk - max) and rounds O once; the split depends only on the

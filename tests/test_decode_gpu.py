@@ -96,8 +96,9 @@ def test_decode_parity_f16(B, H, H_kv, Nq, Nk, causal):
     run_decode_case(dw(B, H, H_kv, Nq, Nk, causal, seed, "f16"))
 
 
-# Other types and head sizes: the generic forward kernel with the cache as
-# its keys (no split).
+# The 16-bit types at d = 64 take the split-cache kernel on 128-byte rows;
+# other types and head sizes the generic forward kernel with the cache as its
+# keys (no split).
 GENERIC_CASES = [
     (2, 4, 2, 1, 700, 64, "bf16", False),
     (1, 6, 3, 5, 300, 64, "f16", True),
@@ -105,6 +106,8 @@ GENERIC_CASES = [
     (1, 3, 3, 16, 16, 16, "f32", True),
     (1, 8, 2, 40, 1000, 128, "f32", False),
     (1, 2, 2, 200, 70, 64, "bf16", False),  # more queries than keys, no mask
+    (4, 16, 2, 1, 9000, 64, "bf16", True),  # long cache: split into chunks
+    (2, 16, 1, 3, 4133, 64, "f16", True),   # 48 rows per key/value head: two row blocks
 ]
 
 

@@ -360,9 +360,10 @@ def test_tuned_and_generic_tilings_agree(dtype, H, H_kv, causal, d, qk_mult, mon
     assert torch.equal(tuned[0], generic[0]) and torch.equal(tuned[1], generic[1])
 
 
-def test_decode_split_and_unsplit_agree(monkeypatch):
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (64, "f16")])
+def test_decode_split_and_unsplit_agree(d, dtype, monkeypatch):
     """Decoding: the split-cache kernel against the unsplit generic path."""
-    w = workloads.DecodeWorkload("tilings_decode", 2, 16, 4, 3, 3000, 128, "bf16", True, 3402)
+    w = workloads.DecodeWorkload("tilings_decode", 2, 16, 4, 3, 3000, d, dtype, True, 3402 + d)
     q, k, v = workloads.make_decode_inputs(w, device="cuda")
     monkeypatch.delenv("FA2_FORCE_GENERIC", raising=False)
     a = fa.decode(q, k, v, True, w.scale)
@@ -370,8 +371,8 @@ def test_decode_split_and_unsplit_agree(monkeypatch):
     b = fa.decode(q, k, v, True, w.scale)
     monkeypatch.delenv("FA2_FORCE_GENERIC")
     torch.cuda.synchronize()
-    assert rel_err(a[0].float().cpu(), b[0].float().cpu()) <= TOL["bf16"]
-    assert rel_err(a[1].cpu(), b[1].cpu()) <= TOL["bf16"]
+    assert rel_err(a[0].float().cpu(), b[0].float().cpu()) <= TOL[dtype]
+    assert rel_err(a[1].cpu(), b[1].cpu()) <= TOL[dtype]
 
 
 # fa2_backward_stage 1, 2, 3 in order is fa2_backward, whichever kernel each

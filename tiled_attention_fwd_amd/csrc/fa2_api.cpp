@@ -33,11 +33,11 @@ bool is_empty(int B, int H, int N) { return B == 0 || H == 0 || N == 0; }
 bool valid_hkv(int H, int H_kv) { return H == 0 ? H_kv >= 0 : (H_kv >= 1 && H % H_kv == 0); }
 
 
-// Decoding splits the cache over workgroups for 16-bit types at d = 128; other
-// types and head sizes run the generic forward kernel, which needs no
-// workspace.
+// Decoding splits the cache over workgroups for 16-bit types at d = 128 and
+// 64; other types and head sizes run the generic forward kernel, which needs
+// no workspace.
 bool decode_split_path(int dtype, int d) {
-  return (dtype == FA2_BF16 || dtype == FA2_F16) && d == 128 && !fa2::force_generic_kernels();
+  return (dtype == FA2_BF16 || dtype == FA2_F16) && (d == 128 || d == 64) && !fa2::force_generic_kernels();
 }
 
 // Packed ragged batches: T rows per head, sequences of at most max_seqlen

@@ -1,5 +1,5 @@
 // fa2_decode.hip -- flash-decoding: a few new queries against a long key/value
-// cache, bf16 or fp16, d = 128.
+// cache, bf16 or fp16, d = 128 or 64.
 //
 // The article "Revolutionizing Web-Based AI: How a Plain JavaScript Prototype
 // Paved the Way for High-Performance WebGPU Flash Attention 2" names
@@ -21,8 +21,8 @@
 // The pass reads the cache once: 2 N_k d s bytes per key/value head against
 // about 4 N_k d flops per row, a few flops per byte, so it is bound by HBM.
 // The kernel is built for bytes in flight: one wave per workgroup with its
-// own 4-slot ring of 32-key K and V blocks (64 KB of LDS, two workgroups per
-// CU), three blocks loaded ahead by direct global-to-LDS loads, and no
+// own 4-slot ring of 32-key K and V blocks (64 KB of LDS at d = 128, two
+// workgroups per CU; 32 KB at d = 64), three blocks loaded ahead by direct global-to-LDS loads, and no
 // barrier at all (a wave only reads what it loaded itself, after its own
 // vmcnt wait).  The products use the forward's layout: S^T = K Q^T so the
 // lane owning a row keeps m and l as scalars, and P is the B operand of
@@ -34,21 +34,21 @@ namespace fa2 {
 namespace {
 
 namespace dec {
-constexpr int D = 128;
 constexpr int KB = 32;           // keys per block
-constexpr int BLK_E = KB * D;    // elements of one K or V block
 constexpr int R = 4, PF = R - 1; // ring slots, blocks loaded ahead
-constexpr int LOADS = BLK_E * 2 / 1024;  // 1-KB direct loads per K (or V) block: 8
+// 1-KB direct loads per K (or V) block: 8 at d = 128, 4 at d = 64.
+constexpr int loads(int D) { return KB * D * 2 / 1024; }
 static_assert(PF >= 1 && PF <= 3, "the waits below are written out for up to 3 blocks ahead");
 }  // namespace dec
 
-// s_waitcnt vmcnt(16 n), expcnt and lgkmcnt at their maxima: all but the
-// last n blocks' loads (2 x 8 per block) done.  vmcnt's low four bits sit in
-// bits 3:0 of the immediate, its high two in bits 15:14.  The empty asm keeps
-// the compiler from moving LDS reads above the wait.
-template <int NBLK>
+// s_waitcnt vmcnt(2 L n), expcnt and lgkmcnt at their maxima: all but the
+// last n blocks' loads (2 x L per block, L = dec::loads(D)) done.  vmcnt's
+// low four bits sit in bits 3:0 of the immediate, its high two in bits
+// 15:14.  The empty asm keeps the compiler from moving LDS reads above the
+// wait.
+template <int D, int NBLK>
 __device__ __forceinline__ void wait_blocks() {
-  constexpr int c = 2 * dec::LOADS * NBLK;
+  constexpr int c = 2 * dec::loads(D) * NBLK;
   static_assert(c < 64, "vmcnt holds 6 bits");
   __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | 0x0F70);
   asm volatile("" ::: "memory");
@@ -60,7 +60,7 @@ __device__ __forceinline__ void wait_blocks() {
 // and LSE; otherwise its normalised O rows (fp32) and base-2 LSE go to
 // PartO[sp], PartL[sp] (LSE = -inf and O = 0 for a row that sees no key of
 // the chunk).
-template <typename T, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                     const T* __restrict__ V, T* __restrict__ O,
                                                     float* __restrict__ LSE, float* __restrict__ PartO,
@@ -68,8 +68,13 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
                                                     int Hkv, int n_rb, int S, int cb, long long rows,
                                                     float sl2) {
   using namespace tiles;
-  constexpr int D = dec::D, KB = dec::KB, BLK_E = dec::BLK_E, R = dec::R, PF = dec::PF;
+  static_assert(D == 128 || D == 64, "decode_kernel: d = 128 or 64");
+  constexpr int KB = dec::KB, BLK_E = KB * D, R = dec::R, PF = dec::PF, LOADS = dec::loads(D);
   constexpr int CH = 8, DCH = D / 16, NB = D / 32;
+  constexpr int ROWB = 2 * D;       // bytes per LDS row
+  constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;  // rows per 1-KB load
+  constexpr int LPP = 16 / RPL;     // loads per 16 rows (the swizzles' period)
   __shared__ __attribute__((aligned(16))) T Ks[R][BLK_E];
   __shared__ __attribute__((aligned(16))) T Vs[R][BLK_E];
 
@@ -94,16 +99,18 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
   const int kb0 = sp * cb;
   const int nb = min(nbk, kb0 + cb) - kb0;  // >= 1: the host leaves no split empty
 
-  // Direct loads: load u of a block brings rows 4u .. 4u+3 (1 KB) into
-  // bytes u*1024 .. of the slot; voff[u & 3] + (u >> 2) * 4096 is the
-  // lane's byte offset in the block (swizzled chunk, as the LDS tile wants).
-  int voff[4];
+  // Direct loads: load u of a block brings rows RPL u .. RPL u + RPL - 1
+  // (1 KB) into bytes u*1024 .. of the slot; voff[u % LPP] + (u / LPP) *
+  // 16 ROWB is the lane's byte offset in the block (swizzled chunk, as the
+  // LDS tile wants; both swizzles repeat every 16 rows).
+  auto swz_row = [](int r) { return D == 128 ? swz(r) : swz64(r); };
+  int voff[LPP];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int rr = 4 * u + (lane >> 4);
-    voff[u] = rr * 256 + (((lane & 15) ^ swz(rr)) << 4);
+  for (int u = 0; u < LPP; ++u) {
+    const int rr = RPL * u + lane / CPR;
+    voff[u] = rr * ROWB + (((lane % CPR) ^ swz_row(rr)) << 4);
   }
-  const SwzOffsets so = swz_offsets(lane);
+  const SwzOffsets so = D == 128 ? swz_offsets(lane) : swz_offsets64(lane);
   int kofs[DCH], vofs0[NB], vofs1[NB];
 #pragma unroll
   for (int c = 0; c < DCH; ++c) kofs[c] = so.rofs ^ (c << 5);
@@ -120,14 +127,16 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
     T* dv = &Vs[slot][0];
     if (row0 + KB <= Nk) {
 #pragma unroll
-      for (int u = 0; u < dec::LOADS; ++u) bload16(rk, voff[u & 3] + (u >> 2) * 4096, row0 * 256, dk + u * 512);
+      for (int u = 0; u < LOADS; ++u)
+        bload16(rk, voff[u % LPP] + (u / LPP) * 16 * ROWB, row0 * ROWB, dk + u * 512);
 #pragma unroll
-      for (int u = 0; u < dec::LOADS; ++u) bload16(rv, voff[u & 3] + (u >> 2) * 4096, row0 * 256, dv + u * 512);
+      for (int u = 0; u < LOADS; ++u)
+        bload16(rv, voff[u % LPP] + (u / LPP) * 16 * ROWB, row0 * ROWB, dv + u * 512);
     } else {
 #pragma unroll
-      for (int u = 0; u < dec::LOADS; ++u) {
-        const int rr = 4 * u + (lane >> 4);
-        const int off = min(row0 + rr, Nk - 1) * 256 + (voff[u & 3] & 255);
+      for (int u = 0; u < LOADS; ++u) {
+        const int rr = RPL * u + lane / CPR;
+        const int off = min(row0 + rr, Nk - 1) * ROWB + (voff[u % LPP] & (ROWB - 1));
         bload16(rk, off, 0, dk + u * 512);
         bload16(rv, off, 0, dv + u * 512);
       }
@@ -157,13 +166,13 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
     const int ahead = nb - 1 - t;  // blocks of the chunk after this one
     if (ahead >= PF) {
       issue(kb0 + t + PF, (SLOT + PF) % R);  // that slot held block t - 1, already consumed
-      wait_blocks<PF>();
+      wait_blocks<D, PF>();
     } else if (ahead == 2) {
-      wait_blocks<2>();
+      wait_blocks<D, 2>();
     } else if (ahead == 1) {
-      wait_blocks<1>();
+      wait_blocks<D, 1>();
     } else {
-      wait_blocks<0>();
+      wait_blocks<D, 0>();
     }
     f32x16 s = f32x16{};
     {
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
       const u32x4 pb = pack_chunk<T>(s, tt);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb)
-        mfma_chunk<T>(o[bb], tr_frag(vb_, vofs0[bb] + tt * 4096, vofs1[bb] + tt * 4096), pb);
+        mfma_chunk<T>(o[bb], tr_frag(vb_, vofs0[bb] + tt * 16 * ROWB, vofs1[bb] + tt * 16 * ROWB), pb);
     }
   };
 
@@ -270,13 +279,12 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
 
 // Merge of the S chunks of each row: with L_s the chunks' base-2 LSE and
 // L* = max_s L_s, w_s = 2^(L_s - L*), O = sum_s w_s O_s / sum_s w_s and
-// LSE = (L* + log2 sum_s w_s) ln 2.  32 threads per row, 4 elements each;
+// LSE = (L* + log2 sum_s w_s) ln 2.  D / 4 threads per row, 4 elements each;
 // every row has at least one chunk with a visible key, so L* is finite.
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ PartO,
                                                            const float* __restrict__ PartL, T* __restrict__ O,
                                                            float* __restrict__ LSE, long long rows, int S) {
-  constexpr int D = dec::D;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = idx / (D / 4);
   const int c = (int)(idx % (D / 4)) * 4;
@@ -297,36 +305,38 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 }  // namespace
 
-template <typename T>
+template <typename T, int D>
 static hipError_t launch_decode_t(const DecArgs& a) {
   const DecodePlan p = decode_plan(a.B, a.H, a.Hkv, a.Nq, a.Nk);
   const long long rows = (long long)a.B * a.H * a.Nq;
   const long long blocks = (long long)a.B * a.Hkv * p.splits * p.row_blocks;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   float* part_o = a.workspace;
-  float* part_l = a.workspace + align256((size_t)p.splits * rows * dec::D * sizeof(float)) / sizeof(float);
+  float* part_l = a.workspace + align256((size_t)p.splits * rows * D * sizeof(float)) / sizeof(float);
   const float sl2 = a.scale * kLog2e;
   const int G = a.H / a.Hkv;
   if (a.causal)
-    hipLaunchKernelGGL((decode_kernel<T, true>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<T*>(a.o), a.lse, part_o, part_l, a.Nq, a.Nk, a.H, G, a.Hkv, p.row_blocks,
                        p.splits, p.chunk_blocks, rows, sl2);
   else
-    hipLaunchKernelGGL((decode_kernel<T, false>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3((unsigned)blocks), dim3(64), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<T*>(a.o), a.lse, part_o, part_l, a.Nq, a.Nk, a.H, G, a.Hkv, p.row_blocks,
                        p.splits, p.chunk_blocks, rows, sl2);
   if (p.splits > 1) {
-    const long long threads = rows * (dec::D / 4);
-    hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, a.stream,
+    const long long threads = rows * (D / 4);
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, a.stream,
                        part_o, part_l, static_cast<T*>(a.o), a.lse, rows, p.splits);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecArgs& a) {
-  return a.dtype == kF16 ? launch_decode_t<_Float16>(a) : launch_decode_t<__bf16>(a);
+  if (a.d == 64) return a.dtype == kF16 ? launch_decode_t<_Float16, 64>(a) : launch_decode_t<__bf16, 64>(a);
+  if (a.d == 128) return a.dtype == kF16 ? launch_decode_t<_Float16, 128>(a) : launch_decode_t<__bf16, 128>(a);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa2

@@ -139,9 +139,11 @@ inline size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
 
 // FA2_FORCE_GENERIC set to anything but "0" in the environment makes every
 // call take the generic kernels (register-staged tiles) instead of the tuned
-// 16-bit d = 128 ones, and decoding the unsplit path: a second, independent
-// tiling of the same arithmetic, for checking the two against each other.
-// Read on the host at every call; no state is kept.
+// 16-bit d = 128 and d = 64 ones, and decoding the unsplit path: a second,
+// independent tiling of the same arithmetic, for checking the two against
+// each other.  Read on the host at every call; no state is kept, so it must
+// not change between the stages of one backward pass (the tuned stage 1
+// computes dQ, the generic stage 3 does).
 inline bool force_generic_kernels() {
   const char* e = getenv("FA2_FORCE_GENERIC");
   return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
@@ -149,7 +151,9 @@ inline bool force_generic_kernels() {
 
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_decode(const DecArgs& a);
-// stage 1: D = rowsum(dO * O); 2: the dK/dV kernel; 3: the dQ kernel.
+// stage 1: D = rowsum(dO * O) (the dQ kernel with D for the tuned 16-bit
+// kernels); 2: the dK/dV kernel; 3: the dQ kernel (nothing after a tuned
+// stage 1).
 hipError_t launch_backward_stage(const BwdArgs& a, int stage);
 
 }  // namespace fa2

@@ -110,7 +110,8 @@ def test_workspace_size_formula(L):
 def test_workspace_size_ex_formula(L):
     """Grouped-query sizes: the plain size, plus fp32 partial dK and dV when a
     bf16 d=128 group is split over S workgroups (S the smallest divisor of G
-    giving 1024 key-tile workgroups, else G)."""
+    giving 1024 key-tile workgroups, else G), or an fp32 key tile's walk over
+    the query tiles is cut into S pieces."""
     def al(x):
         return (x + 255) // 256 * 256
     B, H, N, d = 4, 16, 4096, 128
@@ -124,9 +125,18 @@ def test_workspace_size_ex_formula(L):
     assert L.fa2_backward_workspace_size_ex(1, 8, 1, 64, 128, 1) == 2 * al(8 * 64 * 4) + 2 * al(8 * 64 * 128 * 4)
     # G = 6 with 1 key tile: S runs 2, 3, 6
     assert L.fa2_backward_workspace_size_ex(1, 6, 1, 64, 128, 1) == 2 * al(6 * 64 * 4) + 2 * al(6 * 64 * 128 * 4)
-    # enough workgroups already (16 x 8 x 8 = 1024), fp32, or another head size: no partials
+    # enough workgroups already (16 x 8 x 8 = 1024) or another head size: no partials
     assert L.fa2_backward_workspace_size_ex(8, 16, 8, 2048, d, 1) == 2 * al(8 * 16 * 2048 * 4)
-    assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 0) == plain
+    # fp32 splits query tiles instead, to 512 workgroups while the longest walk
+    # keeps 4 query tiles (32 rows at d >= 64, 64 below) per piece:
+    # 32 key tiles x 4 x 2 = 256 -> S = 2
+    assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 0) == plain + 2 * al(2 * B * 2 * N * d * 4)
+    # the 8x8x512x64 shape: 4 key tiles x 64 = 256 -> S = 2 (walks of 16 query tiles)
+    assert L.fa2_backward_workspace_size(8, 8, 512, 64, 0) == 2 * al(64 * 512 * 4) + 2 * al(2 * 64 * 512 * 64 * 4)
+    # 4x4x256x32: a walk of 4 query tiles is not split
+    assert L.fa2_backward_workspace_size(4, 4, 256, 32, 0) == 2 * al(16 * 256 * 4)
+    # 2048 workgroups already: no split
+    assert L.fa2_backward_workspace_size_ex(8, 16, 16, 2048, d, 0) == 2 * al(8 * 16 * 2048 * 4)
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 2) == plain + 2 * al(4 * B * 2 * N * d * 4)
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, 64, 1) == plain
     assert L.fa2_backward_workspace_size_ex(B, H, 3, N, d, 1) == 0

@@ -142,7 +142,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int Nmax,
-    int BHkv, float sl2, float scale, int H, int G, const int* __restrict__ cu, int Ttot) {
+    int BHkv, float sl2, float scale, int H, int G, const int* __restrict__ cu, int Ttot, int S,
+    float* __restrict__ PartK, float* __restrict__ PartV, long long kv_rows) {
   using C = DkdvTile<T, D>;
   constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB, QS = C::QS;
   // Double-buffered query-side tiles: one barrier per query tile.
@@ -155,7 +156,8 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / BHkv;  // ascending: for causal the heaviest key tiles go first
+  const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
+  const int sp = (lin % (BHkv * S)) / BHkv;  // which of the S pieces of the query-tile walk
   const int bhk = lin % BHkv;  // (sequence, key/value head); it serves query heads hk*G .. hk*G + G - 1
   const int bq = bhk / (H / G), hk = bhk % (H / G);
   const SeqRows skv = seq_rows(cu, Nmax, Ttot, bq, hk, H / G);
@@ -191,7 +193,10 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   }
 
   const int n_qt = (N + BR - 1) / BR;
-  const int qt_begin = CAUSAL ? kv0 / BR : 0;
+  const int qt_first = CAUSAL ? kv0 / BR : 0;
+  // This workgroup's piece of the walk: query tiles [qt_begin, qt_end).
+  const int qt_begin = qt_first + (int)((long long)(n_qt - qt_first) * sp / S);
+  const int qt_end = qt_first + (int)((long long)(n_qt - qt_first) * (sp + 1) / S);
 
   u32x4 qr[C::Q_PER_T], gr[C::Q_PER_T];
   float lr = 0.f, dr = 0.f;
@@ -321,9 +326,9 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
       grad(ls, ds, i0, 1, s1, dp1, BoolC<false>{});
       mm_kv(qs, gs, 1, s1, dp1);
     }
-    if (qt + 1 < n_qt) store_q(buf ^ 1);
+    if (qt + 1 < qt_end) store_q(buf ^ 1);
     __syncthreads();
-    if (qt + 2 < n_qt) load_q(qt + 2);
+    if (qt + 2 < qt_end) load_q(qt + 2);
   };
   // Query tiles that cross this key tile's diagonal band (or every tile when
   // the key tile is ragged) run with the mask; the rest need none.  The walk
@@ -336,15 +341,40 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     dOh = dO + (size_t)qrow0 * D;
     lseh = LSE + qrow0;
     dlh = Delta + qrow0;
-    if (qt_begin < n_qt) {
+    if (qt_begin < qt_end) {
       load_q(qt_begin);
       store_q(0);
-      if (qt_begin + 1 < n_qt) load_q(qt_begin + 1);
+      if (qt_begin + 1 < qt_end) load_q(qt_begin + 1);
     }
     __syncthreads();
     int qt = qt_begin, it = 0;
-    for (; qt < qt_mask_end; ++qt, ++it) iteration(qt, it, BoolC<true>{});
-    for (; qt < n_qt; ++qt, ++it) iteration(qt, it, BoolC<false>{});
+    for (; qt < min(qt_mask_end, qt_end); ++qt, ++it) iteration(qt, it, BoolC<true>{});
+    for (; qt < qt_end; ++qt, ++it) iteration(qt, it, BoolC<false>{});
+  }
+
+  if (S > 1) {
+    // One of S partial sums over the query tiles: fp32 rows of [S][kv_rows,
+    // d], dK already scaled (an empty piece writes zeros);
+    // bwd_dkdv_reduce_kernel adds them up.
+    if (kj < N) {
+      const size_t row = (size_t)sp * kv_rows + skv.row0 + kj;
+      float* pk = PartK + row * D;
+      float* pv = PartV + row * D;
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * b + 8 * g + 4 * h;
+          if (d0 < D) {
+            *reinterpret_cast<f32x4*>(pk + d0) = f32x4{dk[b][4 * g] * scale, dk[b][4 * g + 1] * scale,
+                                                        dk[b][4 * g + 2] * scale, dk[b][4 * g + 3] * scale};
+            *reinterpret_cast<f32x4*>(pv + d0) = f32x4{dv[b][4 * g], dv[b][4 * g + 1], dv[b][4 * g + 2],
+                                                        dv[b][4 * g + 3]};
+          }
+        }
+      }
+    }
+    return;
   }
 
   if (kj < N) {
@@ -1421,12 +1451,23 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   }
   if (stage == 2) {
     using C = DkdvTile<T, D>;
+    // fp32 splits each key tile's query walk (a.splits pieces); the 16-bit
+    // types walk it whole here (their splits are the d = 128 kernel's).
+    const int S = sizeof(T) == 4 ? a.splits : 1;
     const long long blocks = (long long)((a.N + C::BC - 1) / C::BC) * BHkv;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    if (blocks * S > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const long long n = kv_rows * D;  // elements of dK (and of dV)
+    float* part_k = a.part;
+    float* part_v = a.part + align256((size_t)S * n * sizeof(float)) / sizeof(float);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
-                       a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T);
+                       a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T, S, part_k, part_v, kv_rows);
+    if (S > 1) {
+      const unsigned rb = (unsigned)((n / 4 + 255) / 256);
+      hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,
+                         static_cast<T*>(a.dk), static_cast<T*>(a.dv), n, S, a.cu, a.B, a.T, D);
+    }
     return hipGetLastError();
   }
   if (stage == 3) {

@@ -55,7 +55,7 @@ struct BwdArgs {
   float* delta;  // D = rowsum(dO * O), [B, H, N] inside the workspace
   float* lse2;   // LSE * log2(e), [B, H, N] inside the workspace
   float* part;   // splits > 1: fp32 partial dK then dV, [splits][B, Hkv, N, d] each
-  int splits;    // workgroups that share one key/value head's query-head group
+  int splits;    // workgroups that share one key tile (its query heads, or fp32: its query tiles)
   hipStream_t stream;
   const int* cu;  // as FwdArgs
   int T;
@@ -74,8 +74,23 @@ inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return 2 *
 // there are at least 1024 of them (four per CU: with causal masking the key
 // tiles differ in cost, and two per CU left the heavy ones as a tail), and a
 // second kernel sums the S partial results in a fixed order.
+//
+// fp32 runs the generic dK/dV kernel at one workgroup per CU.  There the
+// split is over query tiles instead: when the key tiles leave fewer than
+// 512 workgroups, each key tile's walk over the query tiles is cut into S
+// consecutive pieces (as long as the longest walk keeps at least 4 query
+// tiles per piece), and the same second kernel sums the pieces' partials.
+// With causal masking this also shortens the heaviest workgroup's walk.
 inline int dkdv_splits(int B, int Hkv, int G, int N, int d, int dtype) {
-  if (G <= 1 || d != 128 || dtype == kF32) return 1;
+  if (dtype == kF32) {
+    const int br = d >= 64 ? 32 : 64;  // query rows per step of the fp32 generic kernel
+    const int steps = (N + br - 1) / br;
+    const long long base = (long long)((N + 127) / 128) * B * Hkv;
+    int S = 1;
+    while (base * S < 512 && steps / (S + 1) >= 4) ++S;
+    return S;
+  }
+  if (G <= 1 || d != 128) return 1;
   const long long base = (long long)((N + 127) / 128) * B * Hkv;
   int S = 1;
   while (S < G && base * S < 1024) {

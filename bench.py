@@ -3,9 +3,8 @@
 
 One step = the whole hot path over one batch of the large causal bf16
 workload (B=4, H=16, N=4096, d=128): ``fa2_forward`` and then the three
-backward stages (D = rowsum(dO * O), the dK/dV kernel, the dQ kernel; at
-d = 128 and 64 in the 16-bit types the dQ kernel computes D itself and runs
-as stage 1, and stage 3 is empty), i.e. exactly ``fa2_backward``, called stage
+backward stages (the dQ kernel, which also computes D = rowsum(dO * O); the
+dK/dV kernel; an empty third stage), i.e. exactly ``fa2_backward``, called stage
 by stage so that HIP events on the launch stream can time each kernel.  The default 30 warmup steps let
 the clocks settle; 100 timed steps take about 0.15 s.  Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.
@@ -63,7 +62,6 @@ def counted_flop(w):
 # readings to the kernel version they were taken on).
 KERNEL_SOURCES = {
     "fwd_kernel": ["fa2_fwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
-    "bwd_pre_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
     "bwd_dkdv_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
     "bwd_dq_kernel": ["fa2_bwd.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
     "decode_kernel": ["fa2_decode.hip", "fa2_common.hpp", "fa2_launch.hpp", "fa2_swz.hpp"],
@@ -71,13 +69,10 @@ KERNEL_SOURCES = {
 
 
 def stage_kernels(dtype: str, d: int) -> list:
-    """Kernel names of the forward call and backward stages 1, 2, 3, in order.
-    For the 16-bit types at d = 128 and 64 the dQ kernel computes D and
-    LSE*log2(e) itself and runs as stage 1; stage 3 then enqueues nothing."""
-    generic = os.environ.get("FA2_FORCE_GENERIC", "") not in ("", "0")
-    if dtype in ("bf16", "f16") and d in (128, 64) and not generic:
-        return ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_stage3_empty"]
-    return ["fwd_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    """Kernel names of the forward call and backward stages 1, 2, 3, in order:
+    the dQ kernel computes D and LSE*log2(e) itself and runs as stage 1; stage
+    3 enqueues nothing."""
+    return ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_stage3_empty"]
 
 
 def source_hash(kernel: str) -> str:

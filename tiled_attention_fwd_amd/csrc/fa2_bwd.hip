@@ -13,12 +13,19 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Kernels, in stream order:
-//   bwd_pre_kernel   D = rowsum(dO o O) in fp32 (HBM-bound, one pass over O
-//                    and dO), and LSE * log2(e) for the dK/dV kernel; not
-//                    run where bwd_dq_pp_kernel computes them (below).
-//   bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile); each of
-//                    its 4 waves owns 32 keys and keeps K, V (as MFMA B
-//                    operands) and its dK^T, dV^T accumulators in registers
+//   bwd_dq_kernel    stage 1: one workgroup per (batch, head, 128-query
+//                    tile), shaped like the forward pass: S^T = K Q^T and
+//                    dP^T = V dO^T on MFMA, so each lane owns one query and
+//                    its LSE and D are scalars, then dQ^T += K^T dS^T.  It
+//                    first computes D = rowsum(dO o O) (it holds the lane's
+//                    dO row already and loads its O row) and LSE * log2(e)
+//                    for its rows and writes both to the workspace for the
+//                    dK/dV kernel.  For the 16-bit types at d = 128 and 64,
+//                    bwd_dq_pp_kernel runs the same pass over a ring of
+//                    direct-loaded 32-key blocks, like fwd_pp_kernel.
+//   bwd_dkdv_kernel  stage 2: one workgroup per (batch, head, 128-key tile);
+//                    each of its 4 waves owns 32 keys and keeps K, V (as MFMA
+//                    B operands) and its dK^T, dV^T accumulators in registers
 //                    while it walks the query tiles: S = Q K^T and
 //                    dP = dO V^T on MFMA, P and dS in fp32, then
 //                    dV^T += dO^T P and dK^T += Q^T dS on MFMA, with P and dS
@@ -30,16 +37,10 @@
 //                    bwd_dkdv_d64_kernel does the same at d = 64.
 //                    With grouped-query heads a workgroup walks every query
 //                    head of its key/value head's group (or a 1/S share of
-//                    them, bwd_dkdv_reduce_kernel then summing the S fp32
-//                    partials in a fixed order).
-//   bwd_dq_kernel    one workgroup per (batch, head, 128-query tile), shaped
-//                    like the forward pass: S^T = K Q^T and dP^T = V dO^T on
-//                    MFMA, so each lane owns one query and its LSE and D are
-//                    scalars, then dQ^T += K^T dS^T.  For the 16-bit types
-//                    at d = 128 and 64, bwd_dq_pp_kernel runs it over a ring
-//                    of direct-loaded 32-key blocks, like fwd_pp_kernel, and
-//                    computes D and LSE * log2(e) for its own rows on the
-//                    way (it is then stage 1, ahead of dK/dV).
+//                    them; in fp32, a 1/S share of the query tiles), and
+//                    bwd_dkdv_reduce_kernel sums the S fp32 partials in a
+//                    fixed order.
+//   Stage 3 enqueues nothing (dQ came with stage 1).
 // Every kernel takes its (sequence, head) rows from seq_rows, so fixed-length
 // and packed ragged batches share them.
 // The two halves recompute S and dP instead of exchanging dS, so dQ needs no
@@ -91,26 +92,18 @@ __device__ __forceinline__ float dot_chunk<_Float16>(u32x4 a, u32x4 b) {
   return s;
 }
 
-// D_i = sum_k dO_ik O_ik.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                      const float* __restrict__ LSE, float* __restrict__ Delta,
-                                                      float* __restrict__ Lse2, long long rows) {
-  constexpr int CH = Elt<T>::CH;
-  constexpr int TPR = D / CH;  // threads per row (2..32, a power of two)
-  constexpr int RPB = 256 / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int cc = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    acc = dot_chunk<T>(load16(O + row * D + cc * CH), load16(dO + row * D + cc * CH));
-  }
+// D_i = sum_k dO_ik O_ik for the row a lane pair owns in the dQ kernels.
+// Lane half h holds 16-byte chunks 2c + h (c < DCH) of the row; pc[c] is the
+// dot product of chunk 2c + h.  The chunks are added pairwise at distances
+// DCH/2, DCH/4, .., 1 within the lane, then the two halves' sums with one
+// exchange: a fixed tree, the same for every kernel and launch.
+template <int DCH>
+__device__ __forceinline__ float row_dot(float (&pc)[DCH], int lane) {
 #pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && cc == 0) {
-    Delta[row] = acc;
-    Lse2[row] = LSE[row] * kLog2e;  // base-2 units, as the dK/dV kernel's exponent wants them
-  }
+  for (int o = DCH / 2; o >= 1; o /= 2)
+#pragma unroll
+    for (int c = 0; c < o; ++c) pc[c] = pc[c] + pc[c + o];
+  return pc[0] + swap_halves(pc[0], lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -423,8 +416,9 @@ struct DqTile {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ dO,
-                                                        const float* __restrict__ LSE,
-                                                        const float* __restrict__ Delta, T* __restrict__ dQ, int Nmax,
+                                                        const T* __restrict__ O, const float* __restrict__ LSE,
+                                                        float* __restrict__ Lse2, float* __restrict__ Delta,
+                                                        T* __restrict__ dQ, int Nmax,
                                                         int BH, int num_qt, float sl2, float scale, int H, int G,
                                                         const int* __restrict__ cu, int Ttot) {
   using C = DqTile<T, D>;
@@ -449,10 +443,13 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   const int qw = q0 + 32 * w;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
 
-  // Q and dO rows of this lane (B operands); its LSE (base 2) and D.  Rows
-  // past N read row N-1 and are never stored.
+  // Q and dO rows of this lane (B operands); its LSE (base 2) and D, which
+  // this kernel computes for its own rows and writes to the workspace for
+  // the dK/dV kernel that runs after it.  Rows past N read row N-1 and are
+  // never stored.
   const int qc = min(qi, N - 1);
   u32x4 qf[C::DCH], gf[C::DCH];
+  float pc[C::DCH];
   {
     const size_t off = base + (size_t)qc * D + h * CH;
 #pragma unroll
@@ -460,9 +457,15 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
       qf[c] = load16(Q + off + c * 2 * CH);
       gf[c] = load16(dO + off + c * 2 * CH);
     }
+#pragma unroll
+    for (int c = 0; c < C::DCH; ++c) pc[c] = dot_chunk<T>(load16(O + off + c * 2 * CH), gf[c]);
   }
   const float lse2 = LSE[sq.row0 + qc] * kLog2e;
-  const float dl = Delta[sq.row0 + qc];
+  const float dl = row_dot<C::DCH>(pc, lane);  // D = rowsum(dO * O)
+  if (h == 0 && qi < N) {
+    Delta[sq.row0 + qi] = dl;
+    Lse2[sq.row0 + qi] = lse2;
+  }
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int n_kt = (kv_end + BC - 1) / BC;
@@ -1230,16 +1233,7 @@ __global__ __launch_bounds__(256, dqpp::occupancy(D)) void bwd_dq_pp_kernel(cons
 #pragma unroll
     for (int c = 0; c < DCH; ++c) pc[c] = dot_chunk<T>(load16(O + off + c * 2 * CH), gf[c]);
   }
-  // D = rowsum(dO * O).  Fragment c of this lane is 16-byte chunk 2c + h of
-  // the row; the sums pair chunks as the row-parallel bwd_pre_kernel's
-  // butterfly does (offsets CPR/2 .. 1 over the row's CPR chunks), so both
-  // give the same bits.
-  float dh;
-  if constexpr (D == 128)
-    dh = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
-  else
-    dh = (pc[0] + pc[2]) + (pc[1] + pc[3]);
-  const float dl = dh + swap_halves(dh, lane);
+  const float dl = row_dot<DCH>(pc, lane);  // D = rowsum(dO * O)
   const float lse2 = LSE[sq.row0 + qc] * kLog2e;
   if (h == 0 && qi < N) {
     Delta[sq.row0 + qi] = dl;
@@ -1384,16 +1378,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
   const int BHkv = a.B * a.Hkv;  // dK/dV workgroups run over key/value heads
   const int G = a.H / a.Hkv;     // query heads per key/value head
-  // Rows of the query-side and key-side tensors: [B, H, N] / [B, Hkv, N],
-  // or [H, T] / [Hkv, T] for a packed ragged batch.
-  const long long rows = a.cu ? (long long)a.H * a.T : (long long)BH * a.N;
+  // Rows of the key-side tensors: [B, Hkv, N], or [Hkv, T] for a packed
+  // ragged batch.
   const long long kv_rows = a.cu ? (long long)a.Hkv * a.T : (long long)BHkv * a.N;
   const float sl2 = a.scale * kLog2e;
+  // Stage 1 is the dQ kernel, which also computes D and LSE * log2(e) for
+  // its rows; stage 3 has nothing left to do.
+  if (stage == 3) return hipSuccess;
   if (stage == 1) {
     if constexpr (sizeof(T) == 2 && (D == 128 || D == 64)) {
-      // The dQ kernel computes D and LSE * log2(e) for its own rows, so for
-      // these types and head sizes it is stage 1 and stage 3 has nothing
-      // left to do.
       if (!force_generic_kernels()) {
         const int num_qt = (a.N + 127) / 128;
         const long long blocks = (long long)num_qt * BH;
@@ -1406,14 +1399,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
         return hipGetLastError();
       }
     }
-    constexpr int RPB = 256 / (D / Elt<T>::CH);
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dO), a.lse, a.delta, a.lse2,
-                       rows);
+    using C = DqTile<T, D>;
+    const int num_qt = (a.N + C::BR - 1) / C::BR;
+    const long long blocks = (long long)num_qt * BH;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<const T*>(a.dO), static_cast<const T*>(a.o), a.lse, a.lse2, a.delta,
+                       static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T);
     return hipGetLastError();
   }
-  if constexpr (sizeof(T) == 2 && (D == 128 || D == 64))
-    if (stage == 3 && !force_generic_kernels()) return hipSuccess;  // dQ came with stage 1
   if constexpr (sizeof(T) == 2 && D == 128) {
     // (The generic dK/dV kernel walks whole groups itself, so a forced
     // generic run never splits them and the partial sum does not run.)
@@ -1468,17 +1463,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,
                          static_cast<T*>(a.dk), static_cast<T*>(a.dv), n, S, a.cu, a.B, a.T, D);
     }
-    return hipGetLastError();
-  }
-  if (stage == 3) {
-    using C = DqTile<T, D>;
-    const int num_qt = (a.N + C::BR - 1) / C::BR;
-    const long long blocks = (long long)num_qt * BH;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dq), a.N, BH, num_qt, sl2,
-                       a.scale, a.H, G, a.cu, a.T);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -62,8 +62,9 @@ struct BwdArgs {
 };
 
 // Workspace layout: D = rowsum(dO * O), then LSE * log2(e), each float
-// [B, H, N] padded to 256 B; then, when a grouped-query backward splits each
-// group over several workgroups, their fp32 partial dK and dV.
+// [B, H, N] padded to 256 B (written by the dQ kernel of stage 1); then, when
+// the dK/dV stage splits a key tile's work over several workgroups, their
+// fp32 partial dK and dV.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return 2 * align256(rows * sizeof(float)); }
 
@@ -156,9 +157,7 @@ inline size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
 // call take the generic kernels (register-staged tiles) instead of the tuned
 // 16-bit d = 128 and d = 64 ones, and decoding the unsplit path: a second,
 // independent tiling of the same arithmetic, for checking the two against
-// each other.  Read on the host at every call; no state is kept, so it must
-// not change between the stages of one backward pass (the tuned stage 1
-// computes dQ, the generic stage 3 does).
+// each other.  Read on the host at every call; no state is kept.
 inline bool force_generic_kernels() {
   const char* e = getenv("FA2_FORCE_GENERIC");
   return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
@@ -166,9 +165,8 @@ inline bool force_generic_kernels() {
 
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_decode(const DecArgs& a);
-// stage 1: D = rowsum(dO * O) (the dQ kernel with D for the tuned 16-bit
-// kernels); 2: the dK/dV kernel; 3: the dQ kernel (nothing after a tuned
-// stage 1).
+// stage 1: the dQ kernel, which also writes D = rowsum(dO * O) and
+// LSE * log2(e) to the workspace; 2: the dK/dV kernel; 3: nothing.
 hipError_t launch_backward_stage(const BwdArgs& a, int stage);
 
 }  // namespace fa2

@@ -375,10 +375,10 @@ def test_decode_split_and_unsplit_agree(d, dtype, monkeypatch):
     assert rel_err(a[1].cpu(), b[1].cpu()) <= TOL[dtype]
 
 
-# fa2_backward_stage 1, 2, 3 in order is fa2_backward, whichever kernel each
-# stage enqueues: the dQ kernel with D as stage 1 (16-bit, d = 128 and 64),
-# the row-parallel D pass (other types and head sizes), the split grouped
-# dK/dV with its partial sum (grouped-query at d = 128).
+# fa2_backward_stage 1, 2, 3 in order is fa2_backward, whichever kernels the
+# stages enqueue: the ring or the generic dQ kernel with D as stage 1, the
+# d = 128, d = 64 or generic dK/dV kernel, the split grouped dK/dV with its
+# partial sum (grouped-query at d = 128), the fp32 split query walk.
 @pytest.mark.parametrize("dtype,H,H_kv,d,causal", [("bf16", 4, 4, 128, True), ("f16", 4, 2, 64, False),
                                                   ("f32", 2, 2, 64, True), ("bf16", 8, 1, 128, True),
                                                   ("bf16", 2, 2, 32, False)])

@@ -137,6 +137,12 @@ def test_workspace_size_ex_formula(L):
     assert L.fa2_backward_workspace_size(4, 4, 256, 32, 0) == 2 * al(16 * 256 * 4)
     # 2048 workgroups already: no split
     assert L.fa2_backward_workspace_size_ex(8, 16, 16, 2048, d, 0) == 2 * al(8 * 16 * 2048 * 4)
+    # fp32 dQ splits each query tile's walk over 32-key tiles the same way (8
+    # key tiles per piece at least) into the same area: 1x2x2048x64 has 32
+    # query tiles -> dQ S = 7, dK/dV S = 16 (64-tile walks); the larger of
+    # the two partial sets sizes the area
+    assert L.fa2_backward_workspace_size(1, 2, 2048, 64, 0) == \
+        2 * al(2 * 2048 * 4) + max(2 * al(16 * 2 * 2048 * 64 * 4), al(7 * 2 * 2048 * 64 * 4))
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 2) == plain + 2 * al(4 * B * 2 * N * d * 4)
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, 64, 1) == plain
     assert L.fa2_backward_workspace_size_ex(B, H, 3, N, d, 1) == 0

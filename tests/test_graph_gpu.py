@@ -1,7 +1,7 @@
 """HIP graph capture of the forward and backward passes.
 
 The library allocates nothing and records no memset, so a whole step
-(forward, then the three backward kernels) can be captured into a HIP graph
+(forward, then the backward stages) can be captured into a HIP graph
 (torch.cuda.CUDAGraph on ROCm) and replayed.  The graph is replayed several
 times with unrelated eager work and synchronisations between the replays,
 and every replay must give exactly the bits of the eager calls (the kernels

@@ -401,3 +401,14 @@ def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), staged, full):
         assert torch.equal(a, b), "%s: staged backward differs from fa2_backward" % name
+
+
+# fp32 with few heads and long walks: the dK/dV stage cuts each key tile's
+# walk over the query tiles, and the dQ kernel each query tile's walk over
+# the key tiles, into pieces whose fp32 partial sums a second kernel adds
+# (1x2x2048x64: 16 and 7 pieces; a ragged non-causal length and grouped
+# heads as well).
+@pytest.mark.parametrize("B,H,H_kv,N,causal", [(1, 2, 2, 2048, True), (1, 2, 2, 1500, False), (1, 4, 2, 1200, True)])
+def test_fp32_split_walks(B, H, H_kv, N, causal):
+    w = workloads.custom(B, H, N, 64, "f32", causal, 7300 + N + H_kv, name="f32split", H_kv=H_kv)
+    run_case(w)

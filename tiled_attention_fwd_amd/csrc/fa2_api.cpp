@@ -70,7 +70,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 // `kv_rows` ([B, H, N] and [B, H_kv, N], or [H, T] and [H_kv, T]).
 size_t ws_bytes(int B, int H, int H_kv, int N, int d, int dtype, long long rows, long long kv_rows) {
   const int S = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
-  return fa2::ws_total_bytes((size_t)rows, d, dtype) + fa2::ws_part_bytes(kv_rows, d, S);
+  const int Sq = fa2::dq_splits(B, H, N, d, dtype);
+  return fa2::ws_total_bytes((size_t)rows, d, dtype) + fa2::ws_part_bytes(kv_rows, d, S, rows, Sq);
 }
 
 // Stages stage_first .. stage_last of the backward; N as in forward_impl.
@@ -97,8 +98,9 @@ int backward_impl(int stage_first, int stage_last, const void* q, const void* k,
   float* part = static_cast<float*>(static_cast<void*>(static_cast<char*>(workspace) +
                                                        fa2::ws_total_bytes(rows, d, dtype)));
   const int splits = fa2::dkdv_splits(B, H_kv, H / H_kv, N, d, dtype);
-  fa2::BwdArgs a{q,     k,     v,    o,    dO,     lse,   dq, dk, dv, B, H, N, d, H_kv, scale, causal != 0,
-                 dtype, delta, lse2, part, splits, static_cast<hipStream_t>(stream), cu, T};
+  const int dq_splits = fa2::dq_splits(B, H, N, d, dtype);
+  fa2::BwdArgs a{q,     k,     v,    o,    dO,     lse,       dq, dk, dv, B, H, N, d, H_kv, scale, causal != 0,
+                 dtype, delta, lse2, part, splits, dq_splits, static_cast<hipStream_t>(stream), cu, T};
   for (int s = stage_first; s <= stage_last; ++s)
     if (fa2::launch_backward_stage(a, s) != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;

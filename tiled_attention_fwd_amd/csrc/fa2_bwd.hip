@@ -420,7 +420,8 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
                                                         float* __restrict__ Lse2, float* __restrict__ Delta,
                                                         T* __restrict__ dQ, int Nmax,
                                                         int BH, int num_qt, float sl2, float scale, int H, int G,
-                                                        const int* __restrict__ cu, int Ttot) {
+                                                        const int* __restrict__ cu, int Ttot, int S,
+                                                        float* __restrict__ PartQ, long long rows) {
   using C = DqTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -430,7 +431,8 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
+  const int qt = CAUSAL ? (num_qt - 1 - lin / (BH * S)) : (lin / (BH * S));
+  const int sp = (lin % (BH * S)) / BH;  // which of the S pieces of the key-tile walk
   const int bh = lin % BH;
   const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
   const int N = sq.n;  // this sequence's length
@@ -462,13 +464,16 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   }
   const float lse2 = LSE[sq.row0 + qc] * kLog2e;
   const float dl = row_dot<C::DCH>(pc, lane);  // D = rowsum(dO * O)
-  if (h == 0 && qi < N) {
+  if (sp == 0 && h == 0 && qi < N) {
     Delta[sq.row0 + qi] = dl;
     Lse2[sq.row0 + qi] = lse2;
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int n_kt = (kv_end + BC - 1) / BC;
+  // This workgroup's piece of the walk: key tiles [kt_lo, kt_hi).
+  const int kt_lo = (int)((long long)n_kt * sp / S);
+  const int kt_hi = (int)((long long)n_kt * (sp + 1) / S);
 
   u32x4 kr[C::PER_T], vr[C::PER_T];
   auto load_tile = [&](int kt) {
@@ -498,16 +503,18 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
 #pragma unroll
   for (int b = 0; b < C::NB; ++b) dq[b] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
+  if (kt_lo < kt_hi) {
+    load_tile(kt_lo);
+    store_tile(0);
+  }
   __syncthreads();
 
   auto tile = [&](int kt, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    const bool more = kt + 1 < n_kt;
+    const bool more = kt + 1 < kt_hi;
     if (more) load_tile(kt + 1);
-    const T* ks = Ks[kt & 1];
-    const T* vs = Vs[kt & 1];
+    const T* ks = Ks[(kt - kt_lo) & 1];
+    const T* vs = Vs[(kt - kt_lo) & 1];
     const int kb0 = kt * BC;
     const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
     const int nlive = MASKED ? (last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1)) : C::NJB;
@@ -542,16 +549,35 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
         }
       }
     }
-    if (more) store_tile((kt + 1) & 1);
+    if (more) store_tile((kt + 1 - kt_lo) & 1);
     __syncthreads();
   };
   // Key tiles wholly below every row of this query tile and wholly before N
   // need no mask; the diagonal and ragged tiles come last.
   const int kt_full = min(n_kt, CAUSAL ? min(q0, N) / BC : N / BC);
-  int kt = 0;
-  for (; kt < kt_full; ++kt) tile(kt, BoolC<false>{});
-  for (; kt < n_kt; ++kt) tile(kt, BoolC<true>{});
+  int kt = kt_lo;
+  for (; kt < min(kt_full, kt_hi); ++kt) tile(kt, BoolC<false>{});
+  for (; kt < kt_hi; ++kt) tile(kt, BoolC<true>{});
 
+  if (S > 1) {
+    // One of S partial sums over the key tiles, scaled, as fp32 rows of
+    // [S][rows, d] (an empty piece writes zeros); bwd_dkdv_reduce_kernel adds
+    // them up.
+    if (qi < N) {
+      float* pq = PartQ + ((size_t)sp * rows + sq.row0 + qi) * D;
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * b + 8 * g + 4 * h;
+          if (d0 < D)
+            *reinterpret_cast<f32x4*>(pq + d0) = f32x4{dq[b][4 * g] * scale, dq[b][4 * g + 1] * scale,
+                                                        dq[b][4 * g + 2] * scale, dq[b][4 * g + 3] * scale};
+        }
+      }
+    }
+    return;
+  }
   if (qi < N) {
     T* dQi = dQ + base + (size_t)qi * D;
 #pragma unroll
@@ -1400,13 +1426,23 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       }
     }
     using C = DqTile<T, D>;
+    // fp32 splits each query tile's key walk (a.dq_splits pieces).
+    const int S = sizeof(T) == 4 ? a.dq_splits : 1;
     const int num_qt = (a.N + C::BR - 1) / C::BR;
     const long long blocks = (long long)num_qt * BH;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    if (blocks * S > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const long long rows = a.cu ? (long long)a.H * a.T : (long long)BH * a.N;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), static_cast<const T*>(a.o), a.lse, a.lse2, a.delta,
-                       static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T);
+                       static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T, S, a.part, rows);
+    if (S > 1) {
+      const long long n = rows * D;
+      const unsigned rb = (unsigned)((n / 4 + 255) / 256);
+      // (blockIdx.y = 0 only: the partial dQ sums into dq.)
+      hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 1), dim3(256), 0, a.stream, a.part, a.part,
+                         static_cast<T*>(a.dq), static_cast<T*>(a.dq), n, S, a.cu, a.B, a.T, D);
+    }
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2 && D == 128) {

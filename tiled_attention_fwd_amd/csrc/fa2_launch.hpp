@@ -54,8 +54,11 @@ struct BwdArgs {
   int dtype;
   float* delta;  // D = rowsum(dO * O), [B, H, N] inside the workspace
   float* lse2;   // LSE * log2(e), [B, H, N] inside the workspace
-  float* part;   // splits > 1: fp32 partial dK then dV, [splits][B, Hkv, N, d] each
+  float* part;   // splits > 1: fp32 partial dK then dV, [splits][B, Hkv, N, d] each;
+                 // dq_splits > 1: fp32 partial dQ, [dq_splits][B, H, N, d] (stage 1,
+                 // before stage 2 reuses the area)
   int splits;    // workgroups that share one key tile (its query heads, or fp32: its query tiles)
+  int dq_splits; // fp32: workgroups that share one query tile's walk over the key tiles
   hipStream_t stream;
   const int* cu;  // as FwdArgs
   int T;
@@ -100,9 +103,25 @@ inline int dkdv_splits(int B, int Hkv, int G, int N, int d, int dtype) {
   }
   return S;
 }
-// kv_rows: rows of dK ([B, Hkv, N] or, packed, [Hkv, T]).
-inline size_t ws_part_bytes(long long kv_rows, int d, int S) {
-  return S > 1 ? 2 * align256((size_t)S * kv_rows * d * sizeof(float)) : 0;
+// The same split on the dQ side (fp32, generic kernel at one workgroup per
+// CU): with fewer than 512 query-tile workgroups, each query tile's walk
+// over the 32-key tiles is cut into S pieces while the longest walk keeps at
+// least 8 key tiles per piece (shorter walks do not pay for the second
+// launch); a second kernel sums the fp32 partial dQ.
+inline int dq_splits(int B, int H, int N, int d, int dtype) {
+  if (dtype != kF32) return 1;
+  const int steps = (N + 31) / 32;
+  const long long base = (long long)((N + 127) / 128) * B * H;
+  int S = 1;
+  while (base * S < 512 && steps / (S + 1) >= 8) ++S;
+  return S;
+}
+// kv_rows: rows of dK ([B, Hkv, N] or, packed, [Hkv, T]); rows: rows of dQ.
+// Stage 1's partial dQ and stage 2's partial dK, dV share one area.
+inline size_t ws_part_bytes(long long kv_rows, int d, int S, long long rows = 0, int Sq = 1) {
+  const size_t kv = S > 1 ? 2 * align256((size_t)S * kv_rows * d * sizeof(float)) : 0;
+  const size_t q = Sq > 1 ? align256((size_t)Sq * rows * d * sizeof(float)) : 0;
+  return kv > q ? kv : q;
 }
 
 // Decoding (bf16 or fp16, d = 128): N_q queries [B, H, N_q, d] against a cache

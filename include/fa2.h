@@ -81,8 +81,11 @@ int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse
 /*
  * Bytes of device workspace fa2_backward needs for this problem (0 for an
  * empty one).  The workspace holds D = rowsum(dO * O) and LSE * log2(e),
- * each float [B,H,N] padded to 256 bytes; its contents on entry do not
- * matter and on return are unspecified.  Returns 0 for invalid sizes.
+ * each float [B,H,N] padded to 256 bytes, and, in fp32 when the problem
+ * leaves few workgroups for long key or query ranges, fp32 partial sums of
+ * dK, dV or dQ whose ranges were split over several workgroups (added in a
+ * fixed order).  Its contents on entry do not matter and on return are
+ * unspecified.  Returns 0 for invalid sizes.
  */
 size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype);
 
@@ -90,13 +93,14 @@ size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype);
  * Backward pass for the loss L = sum(O * dO).  o and lse must be the outputs
  * of fa2_forward for the same q, k, v, scale and causal.  Overwrites dq, dk,
  * dv (never accumulates into them).  Kernels, in stream order:
- *   1. D_i = sum_k dO_ik O_ik (fp32) and LSE_i * log2(e), into the workspace;
+ *   1. a query-tile-parallel kernel that computes D_i = sum_k dO_ik O_ik
+ *      (fp32) and LSE_i * log2(e) for its rows into the workspace, then
+ *      recomputes P and dP and accumulates dQ in registers;
  *   2. a key-tile-parallel kernel that recomputes P from q, k and lse and
- *      accumulates dK and dV in registers;
- *   3. a query-tile-parallel kernel that recomputes P and dP and accumulates
- *      dQ in registers.
- * No atomics: every output element is written once by one workgroup, so
- * the results are the same bits from run to run.
+ *      accumulates dK and dV in registers.
+ * No atomics: every output element is written once by one workgroup, or
+ * summed from fp32 partials in a fixed order, so the results are the same
+ * bits from run to run.
  * workspace / workspace_bytes: device buffer of at least
  * fa2_backward_workspace_size(B, H, N, d, dtype) bytes, 16-byte aligned.
  */

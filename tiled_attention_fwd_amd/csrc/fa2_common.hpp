@@ -259,6 +259,20 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 // cu[b+1] - cu[b] rows.  Offsets are clamped to [0, T] and the length to
 // Nmax, so inconsistent offsets give wrong rows but never an access outside
 // the tensors.
+// Non-causal tiles all cost the same, so a grid may visit a head's tiles
+// together: workgroups are dealt to the 8 XCDs round-robin, and this order
+// gives XCD x the tiles of heads x, x+8, ... one head after the other, so
+// the K/V rows all of a head's query tiles read stay in that XCD's L2.
+// (Causal grids keep the heaviest-first order instead.)
+struct TileIdx {
+  int tile, head;
+};
+__device__ __forceinline__ TileIdx xcd_head_major(int lin, int heads, int tiles) {
+  if (heads % 8 != 0) return TileIdx{lin / heads, lin % heads};
+  const int x = lin % 8, s = lin / 8;
+  return TileIdx{s % tiles, (s / tiles) * 8 + x};
+}
+
 struct SeqRows {
   long long row0;
   int n;

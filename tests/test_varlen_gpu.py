@@ -79,6 +79,10 @@ VARLEN_CASES = [
     # grouped heads in fp32 at d = 128 (generic kernels), and fp16 at d = 64
     ([300, 1, 129, 77], 4, 2, 128, "f32", True),
     ([513, 31], 6, 3, 64, "f16", True),
+    # fp32 with a long sequence: the dK/dV and dQ walks split into pieces whose
+    # partial sums are added over the packed rows only
+    ([2000, 300, 0, 1100], 2, 2, 64, "f32", True),
+    ([1700, 5, 900], 4, 2, 64, "f32", False),
 ]
 
 

@@ -30,10 +30,11 @@
  *     Calls only enqueue work and return; results are valid once the stream
  *     has completed it.  Calls are reentrant and thread-safe.
  *
- * Kernel choice: the 16-bit types at d = 128 run tuned kernels; with the
- * environment variable FA2_FORCE_GENERIC set (to anything but "0") every
- * call takes the generic kernels instead, a second tiling of the same
- * arithmetic (read at each call; meant for cross-checking the two).
+ * Kernel choice: the 16-bit types at d = 128 and d = 64 run tuned kernels
+ * (direct loads into swizzled LDS rings); with the environment variable
+ * FA2_FORCE_GENERIC set (to anything but "0") every call takes the generic
+ * kernels instead, a second tiling of the same arithmetic (read at each
+ * call; meant for cross-checking the two).
  *
  * Errors: every call returns an fa2_status and never aborts.  Arguments are
  * validated before any HIP call is made, so a rejected call touches no

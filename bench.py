@@ -2,11 +2,11 @@
 """FlashAttention-2 forward + backward throughput on one MI355X.
 
 One step = the whole hot path over one batch of the large causal bf16
-workload (B=4, H=16, N=4096, d=128): ``fa2_forward`` and then the three
-backward stages (the dQ kernel, which also computes D = rowsum(dO * O); the
-dK/dV kernel; an empty third stage), i.e. exactly ``fa2_backward``, called stage
-by stage so that HIP events on the launch stream can time each kernel.  The default 30 warmup steps let
-the clocks settle; 100 timed steps take about 0.15 s.  Inputs are seeded synthetic tensors
+workload (B=4, H=16, N=4096, d=128): ``fa2_forward`` and then the two
+backward stages (the dQ kernel, which also computes D; the dK/dV kernel),
+i.e. exactly ``fa2_backward``, called stage by stage so that HIP events on
+the launch stream can time each kernel.  The default 30 warmup steps let the
+clocks settle; 100 timed steps take about 0.15 s.  Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.
 
 Counted FLOP (causal halves it): forward 4*B*H*N^2*d/2, backward 2.5x that
@@ -69,10 +69,9 @@ KERNEL_SOURCES = {
 
 
 def stage_kernels(dtype: str, d: int) -> list:
-    """Kernel names of the forward call and backward stages 1, 2, 3, in order:
-    the dQ kernel computes D and LSE*log2(e) itself and runs as stage 1; stage
-    3 enqueues nothing."""
-    return ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_stage3_empty"]
+    """Kernel names of the forward call and backward stages 1 and 2, in order:
+    the dQ kernel computes D and LSE*log2(e) itself and runs as stage 1."""
+    return ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]
 
 
 def source_hash(kernel: str) -> str:
@@ -260,7 +259,7 @@ def bench_decode(args) -> int:
 
 
 def bench_varlen(args) -> int:
-    """One step of a packed ragged batch: fa2_forward_varlen and the three
+    """One step of a packed ragged batch: fa2_forward_varlen and the two
     backward stages; counted FLOP summed over the sequences (4 H n^2 d per
     sequence forward, halved when causal; backward 2.5x, step 3.5x)."""
     import torch
@@ -284,13 +283,13 @@ def bench_varlen(args) -> int:
         if evs:
             evs[0].record(stream)
         fa.fa2_forward_varlen(q, k, v, o, lse, cu, w.max_seqlen, w.causal, w.scale, stream)
-        for s in (1, 2, 3):
+        for s in (1, 2):
             if evs:
                 evs[s].record(stream)
             fa.fa2_backward_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu, w.max_seqlen, w.causal, w.scale, ws,
                                    stream, stage=s)
         if evs:
-            evs[4].record(stream)
+            evs[3].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -302,7 +301,7 @@ def bench_varlen(args) -> int:
         step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / K
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for s in range(K):
         step(events[s])
     torch.cuda.synchronize()
@@ -395,12 +394,12 @@ def main() -> int:
         if evs:
             evs[0].record(stream)
         fwd_call(q, k, v, o, lse, w.causal, w.scale, stream)
-        for s in (1, 2, 3):
+        for s in (1, 2):
             if evs:
                 evs[s].record(stream)
             stage_call(s, q, k, v, o, dO, lse, dq, dk, dv, w.causal, w.scale, ws, stream)
         if evs:
-            evs[4].record(stream)
+            evs[3].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -418,7 +417,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for s in range(K):
         step(events[s])
     torch.cuda.synchronize()
@@ -451,7 +450,7 @@ def main() -> int:
                    "seed": w.seed if args.seed is None else args.seed},
         "roofline": roofline,
     }
-    step_ms = sorted(events[s][0].elapsed_time(events[s][4]) for s in range(K))
+    step_ms = sorted(events[s][0].elapsed_time(events[s][3]) for s in range(K))
     detail = {
         "step_events_median_ms": statistics.median(step_ms), "step_events_min_ms": step_ms[0],
         "fwd": {"ms": mean_ms["fwd_kernel"], "tflops": fwd_f / (mean_ms["fwd_kernel"] * 1e-3) / 1e12},
@@ -476,7 +475,7 @@ def main() -> int:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             fwd_call(q, k, v, o, lse, w.causal, w.scale)
-            for st in (1, 2, 3):
+            for st in (1, 2):
                 stage_call(st, q, k, v, o, dO, lse, dq, dk, dv, w.causal, w.scale, ws)
         for _ in range(args.warmup):
             graph.replay()

@@ -112,12 +112,11 @@ int fa2_backward(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * One stage of fa2_backward, with exactly fa2_backward's arguments and
- * checks: stage 1 = the dQ kernel (writes dq, and D = rowsum(dO * O) and
- * LSE * log2(e) of every row to the workspace), 2 = the dK/dV kernel (reads
- * them; writes dk, dv), 3 = nothing (kept so that stages 1, 2, 3 in order
- * remain fa2_backward).  Enqueuing stages 1, 2, 3 in order on one stream is
- * fa2_backward; the split lets a caller record events around each kernel.
- * Any other stage: FA2_ERR_INVALID_ARG.
+ * checks: stage 1 = the dQ kernel (writes dq, and D and LSE * log2(e) of
+ * every row to the workspace), 2 = the dK/dV kernel (reads them; writes dk,
+ * dv).  Enqueuing stages 1 and 2 in order on one stream is fa2_backward; the
+ * split lets a caller record events around each kernel.  Any other stage:
+ * FA2_ERR_INVALID_ARG.
  */
 int fa2_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                        const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,

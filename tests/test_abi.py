@@ -172,7 +172,7 @@ def test_python_binding_rejects_cpu_tensors():
         fa.forward(q, q, q)
 
 
-@pytest.mark.parametrize("stage", [0, 4, -1])
+@pytest.mark.parametrize("stage", [0, 3, 4, -1])
 def test_backward_stage_rejects_bad_stage(L, stage):
     n = L.fa2_backward_workspace_size(1, 2, 64, 64, 1)
     assert L.fa2_backward_stage(stage, A, A, A, A, A, A, A, A, A, 1, 2, 64, 64, 0.125, 1, 1, A, n, None) \

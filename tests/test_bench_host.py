@@ -38,8 +38,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_stage_kernels():
     for dtype, d in (("bf16", 128), ("f16", 64), ("f32", 64), ("bf16", 32)):
-        assert bench.stage_kernels(dtype, d) == ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel",
-                                                 "bwd_stage3_empty"]
+        assert bench.stage_kernels(dtype, d) == ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]
 
 
 def test_stored_traffic_is_tied_to_the_sources(tmp_path, monkeypatch):

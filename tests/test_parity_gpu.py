@@ -15,6 +15,8 @@ kernels fail to write shows up as NaN), and sits inside a larger allocation
 whose guard bands are checked afterwards (an out-of-bounds write at a ragged
 tail changes them).
 """
+import json
+import os
 import sys
 
 import numpy as np
@@ -107,6 +109,11 @@ def run_case(w, heads=None):
     outs = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
     errs = check_against_oracle(w, q, k, v, dO, outs, heads)
     log("  errors: " + " ".join("%s=%.3g" % kv for kv in errs.items()))
+    record = os.environ.get("FA2_PARITY_RECORD")
+    if record:  # one JSON line per compared case, for the measurement notes
+        with open(record, "a") as f:
+            f.write(json.dumps({"case": w.describe(), "seed": w.seed, "heads": "all" if heads is None else heads,
+                                "errors": errs}) + "\n")
     tol = TOL[w.dtype]
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, "%s exceeds tolerance %g: %r" % (w.describe(), tol, bad)
@@ -118,19 +125,21 @@ def test_named_workload_full(wid):
     run_case(workloads.WORKLOADS[wid])
 
 
-def test_ragged_noncausal_bf16_sampled_heads():
-    w = workloads.WORKLOADS[5]
-    run_case(w, heads=[(0, 0), (3, 7), (9, 2), (15, 11)])
+# Workloads 4 and 5 (and the large grouped-query and fp16 variants) are
+# compared whole, every head against the oracle (about 18 s of oracle work
+# per large workload on 16 host threads), in the launch configuration the
+# benchmark times.
+def test_ragged_noncausal_bf16_full():
+    run_case(workloads.WORKLOADS[5])
 
 
-def test_large_causal_bf16_sampled_heads():
-    w = workloads.WORKLOADS[4]
-    run_case(w, heads=[(0, 0), (2, 9), (3, 15)])
+def test_large_causal_bf16_full():
+    run_case(workloads.WORKLOADS[4])
 
 
-def test_large_causal_f16_sampled_heads():
+def test_large_causal_f16_full():
     """The large causal shape in IEEE half precision (workload 7)."""
-    run_case(workloads.WORKLOADS[7], heads=[(0, 0), (1, 6), (3, 15)])
+    run_case(workloads.WORKLOADS[7])
 
 
 def test_ragged_noncausal_f16_stress_sampled_heads():
@@ -140,7 +149,7 @@ def test_ragged_noncausal_f16_stress_sampled_heads():
     run_case(w, heads=[(0, 0), (7, 5), (15, 11)])
 
 
-EDGE_N = [1, 2, 17, 63, 64, 65, 127, 129, 1000]
+EDGE_N = [1, 2, 3, 5, 8, 17, 31, 32, 33, 63, 64, 65, 127, 129, 1000]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
@@ -151,6 +160,34 @@ def test_edge_shapes(N, d, causal, dtype):
     seed = 1000 + N * 7 + d + (1 if causal else 0) + (2 if dtype == "bf16" else 0)
     w = workloads.custom(1, 2, N, d, dtype, causal, seed, name="edge")
     run_case(w)
+
+
+# Causal N = 2 seeds on which D = rowsum(dO o O) from the stored 16-bit O
+# takes dQ or dK past the limit (a CPU model of that rounding,
+# tests/test_short_row_rounding.py, finds them); with D from the first key
+# block they pass.  Both tilings run them.
+@pytest.mark.parametrize("generic", [False, True])
+@pytest.mark.parametrize("dtype,d,seed", [("bf16", 64, 90), ("bf16", 128, 17), ("f16", 64, 7)])
+def test_short_rows_named_seeds(dtype, d, seed, generic, monkeypatch):
+    if generic:
+        monkeypatch.setenv("FA2_FORCE_GENERIC", "1")
+    else:
+        monkeypatch.delenv("FA2_FORCE_GENERIC", raising=False)
+    run_case(workloads.custom(1, 2, 2, d, dtype, True, seed, name="short"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N", [2, 3, 5, 8])
+def test_short_rows_many_seeds(N, dtype):
+    """Forty seeds per short length through the tuned d = 128 kernels."""
+    errs = []
+    for seed in range(40):
+        w = workloads.custom(1, 2, N, 128, dtype, True, 5000 + seed, name="short")
+        q, k, v, dO = workloads.make_inputs(w, device="cuda")
+        outs = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
+        errs.append(max(check_against_oracle(w, q, k, v, dO, outs).values()))
+    log("  N=%d %s worst over 40 seeds: %.3g" % (N, dtype, max(errs)))
+    assert max(errs) <= TOL[dtype]
 
 
 def test_large_logits_causal_bf16():
@@ -299,13 +336,12 @@ def test_mqa_long_bf16():
     run_case(workloads.custom(1, 8, 2049, 128, "bf16", True, 3101, name="mqa", H_kv=1))
 
 
-def test_gqa_bench_workload_sampled_heads():
+def test_gqa_bench_workload_full():
     """The grouped-query workload at full size (4 x 16 query heads over 2
     key/value heads, N = 4096, d = 128, causal bf16), as the benchmark runs
     it: its dK/dV stage splits each group of 8 over 4 workgroups of 2 heads
-    and sums the partials.  Two key/value heads, with their 8 query heads
-    each, against the oracle."""
-    run_case(workloads.WORKLOADS[6], heads=[(0, 0), (3, 1)])
+    and sums the partials.  Every head against the oracle."""
+    run_case(workloads.WORKLOADS[6])
 
 
 def test_gqa_unsplit_sampled_heads():
@@ -396,7 +432,7 @@ def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
     fa.fa2_backward_ex(q, k, v, o, dO, lse, *full, causal, w.scale, ws)
     staged = [torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))]
     ws.fill_(0xFF)
-    for st in (1, 2, 3):
+    for st in (1, 2):
         fa.fa2_backward_stage_ex(st, q, k, v, o, dO, lse, *staged, causal, w.scale, ws)
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), staged, full):
@@ -412,3 +448,33 @@ def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
 def test_fp32_split_walks(B, H, H_kv, N, causal):
     w = workloads.custom(B, H, N, 64, "f32", causal, 7300 + N + H_kv, name="f32split", H_kv=H_kv)
     run_case(w)
+
+
+def test_internal_workspace_on_a_side_stream():
+    """Backward and decoding enqueued on a side stream with no workspace
+    passed: the binding allocates the workspace itself and must keep its
+    memory for the side stream's kernels while the current stream allocates
+    blocks of the same size and fills them.  Results must equal those of
+    the same calls on the current stream, bit for bit."""
+    w = workloads.custom(2, 8, 1000, 128, "bf16", True, 8101, name="side", H_kv=2)
+    log("case: %s seed=%d" % (w.describe(), w.seed))
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    o, lse = fa.forward(q, k, v, True, w.scale)
+    ref = fa.backward(q, k, v, o, lse, dO, True, w.scale)
+    dw = workloads.DecodeWorkload("side_decode", 4, 16, 4, 2, 6000, 128, "bf16", True, 8102)
+    dq_, dk_, dv_ = workloads.make_decode_inputs(dw, device="cuda")
+    dref = fa.decode(dq_, dk_, dv_, True, dw.scale)
+    torch.cuda.synchronize()
+    nb = fa.fa2_backward_workspace_size_ex(w.B, w.H, w.kv_heads, w.N, w.d, q.dtype)
+    nd = fa.fa2_decode_workspace_size(dw.B, dw.H, dw.H_kv, dw.N_q, dw.N_k, dw.d, dq_.dtype)
+    assert nb > 0 and nd > 0
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    outs = fa.backward(q, k, v, o, lse, dO, True, w.scale, stream=side)
+    douts = fa.decode(dq_, dk_, dv_, True, dw.scale, stream=side)
+    junk = [torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda") for n in (nb, nd) for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    for name, a, b in zip(("dQ", "dK", "dV", "O", "LSE"), tuple(outs) + tuple(douts), tuple(ref) + tuple(dref)):
+        assert torch.equal(a, b), "%s differs when enqueued on a side stream" % name

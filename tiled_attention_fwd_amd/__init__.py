@@ -121,6 +121,28 @@ def _stream(stream, device) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """A device buffer that the library's kernels use on ``stream``.
+
+    torch's caching allocator ties a block to the stream current at
+    allocation; when the launch stream is another one, the block is also
+    recorded on it, so that freeing the tensor (at the end of the call that
+    allocated it) cannot hand the memory to new work while the kernels
+    enqueued on ``stream`` still use it."""
+    t = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    _record(t, stream)
+    return t
+
+
+def _record(t: torch.Tensor, stream) -> None:
+    if stream is None:
+        return
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=t.device)
+    if stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -194,7 +216,9 @@ def fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True, scale:
 def fa2_backward_stage(stage: int, q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True,
                        scale: float | None = None, workspace: torch.Tensor | None = None,
                        stream=None) -> None:
-    """Enqueue one backward stage (1: D and LSE*log2(e), 2: dK/dV, 3: dQ)."""
+    """Enqueue one backward stage: 1 the dQ kernel (which also writes D and
+    LSE*log2(e) to the workspace), 2 the dK/dV kernel; 1 then 2 is
+    ``fa2_backward``."""
     if workspace is None:
         raise ValueError("the stages share state through the workspace: pass one")
     _backward_call(False, int(stage), q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
@@ -220,7 +244,7 @@ def _backward_call(ex, stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, wo
         raise ValueError("lse must be float32 [B, H, N]")
     need = fa2_backward_workspace_size_ex(B, H, H_kv, N, d, q.dtype)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     tail = (N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype), workspace.data_ptr(),
@@ -280,7 +304,7 @@ def fa2_backward_workspace_size_varlen(B: int, H: int, H_kv: int, T: int, max_se
 def fa2_backward_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, max_seqlen: int, causal: bool = True,
                         scale: float | None = None, workspace: torch.Tensor | None = None, stream=None,
                         stage: int = 0) -> None:
-    """Backward pass of a packed ragged batch (stage 0: all three kernels,
+    """Backward pass of a packed ragged batch (stage 0: both stages,
     else ``fa2_backward_stage_varlen``); dk, dv have k's shape."""
     _check_tensors_any(q, k, v, o, dO, lse, dq, dk, dv)
     B, H, H_kv, T, d = _varlen_shapes(q, k, v, cu_seqlens, max_seqlen, o, dO, dq)
@@ -292,7 +316,7 @@ def fa2_backward_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, max_seqlen:
     if workspace is None:
         if stage:
             raise ValueError("the stages share state through the workspace: pass one")
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(), dq.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(), B, H, H_kv, T, int(max_seqlen), d,
             _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype), workspace.data_ptr(),
@@ -341,7 +365,7 @@ def fa2_decode(q, k, v, o, lse, causal: bool = False, scale: float | None = None
     code = _dtype_code(q.dtype)
     need = int(lib().fa2_decode_workspace_size(B, H, H_kv, Nq, Nk, d, code))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().fa2_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, Nq,
@@ -357,6 +381,8 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, stream=Non
     B, H, Nq, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    for t in (o, lse):
+        _record(t, stream)
     fa2_decode(q, k, v, o, lse, causal, scale, None, stream)
     return o, lse
 
@@ -367,6 +393,8 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, stream=Non
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for t in (o, lse):
+        _record(t, stream)
     fa2_forward_ex(q, k, v, o, lse, causal, scale, stream)
     return o, lse
 
@@ -376,5 +404,7 @@ def backward(q, k, v, o, lse, dO, causal: bool = True, scale: float | None = Non
     """Return (dq, dk, dv) of L = sum(o * dO); o, lse come from ``forward``;
     dk, dv have k's shape."""
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for t in (dq, dk, dv):
+        _record(t, stream)
     fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
     return dq, dk, dv

@@ -166,7 +166,7 @@ int fa2_backward(const void* q, const void* k, const void* v, const void* o, con
 int fa2_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                     void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, workspace,
+  return backward_impl(1, 2, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, workspace,
                        workspace_bytes, stream);
 }
 
@@ -176,7 +176,7 @@ int fa2_backward_varlen(const void* q, const void* k, const void* v, const void*
                         size_t workspace_bytes, void* stream) {
   const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
   if (st != FA2_OK) return st;
-  return backward_impl(1, 3, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal, dtype,
+  return backward_impl(1, 2, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal, dtype,
                        workspace, workspace_bytes, stream, cu_seqlens, T);
 }
 
@@ -191,7 +191,7 @@ int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v
                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
                           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
+  if (stage < 1 || stage > 2) return FA2_ERR_INVALID_ARG;
   return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype,
                        workspace, workspace_bytes, stream);
 }
@@ -201,7 +201,7 @@ int fa2_backward_stage_varlen(int stage, const void* q, const void* k, const voi
                               const int* cu_seqlens, int B, int H, int H_kv, int T, int max_seqlen, int d,
                               float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  if (stage < 1 || stage > 3) return FA2_ERR_INVALID_ARG;
+  if (stage < 1 || stage > 2) return FA2_ERR_INVALID_ARG;
   const int st = check_varlen(cu_seqlens, B, T, max_seqlen, d);
   if (st != FA2_OK) return st;
   return backward_impl(stage, stage, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, max_seqlen, d, scale, causal,

@@ -106,6 +106,21 @@ __device__ __forceinline__ float row_dot(float (&pc)[DCH], int lane) {
   return pc[0] + swap_halves(pc[0], lane);
 }
 
+// D_i = sum_j P_ij dP_ij over one 32-key block in accumulator layout (this
+// lane's 16 keys of its query, then the other lane half's 16): D in the
+// softmax-Jacobian form, from the fp32 weights and dP before any rounding.
+// A row whose visible keys all lie in its first 32-key block takes this D in
+// place of rowsum(dO o O): with the stored 16-bit O that sum carries O's
+// rounding (relative 2^-9 for bf16), and with one or two keys dP - D is as
+// small as that error, so dS, dQ and dK would inherit it at full size.
+// Longer rows average it away.  Fixed order: r = 0..15, then the halves.
+__device__ __forceinline__ float block_pdp_sum(const f32x16& p, const f32x16& dp, int lane) {
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s = fmaf(p[r], dp[r], s);
+  return s + swap_halves(s, lane);
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (batch, head, 128-key tile).
 // ---------------------------------------------------------------------------
@@ -463,17 +478,18 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
     for (int c = 0; c < C::DCH; ++c) pc[c] = dot_chunk<T>(load16(O + off + c * 2 * CH), gf[c]);
   }
   const float lse2 = LSE[sq.row0 + qc] * kLog2e;
-  const float dl = row_dot<C::DCH>(pc, lane);  // D = rowsum(dO * O)
-  if (sp == 0 && h == 0 && qi < N) {
-    Delta[sq.row0 + qi] = dl;
-    Lse2[sq.row0 + qi] = lse2;
-  }
+  float dl = row_dot<C::DCH>(pc, lane);  // D = rowsum(dO * O)
+  // Rows whose visible keys all lie in keys 0..31 take D = sum_j P_ij dP_ij
+  // from that first 32-key block instead (block_pdp_sum).
+  const bool d_from_block = (CAUSAL ? min(qi, N - 1) : N - 1) < 32;
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int n_kt = (kv_end + BC - 1) / BC;
-  // This workgroup's piece of the walk: key tiles [kt_lo, kt_hi).
+  // This workgroup's piece of the walk: key tiles [kt_lo, kt_hi).  The one
+  // piece that walks key tile 0 writes D and LSE * log2(e) of these rows.
   const int kt_lo = (int)((long long)n_kt * sp / S);
   const int kt_hi = (int)((long long)n_kt * (sp + 1) / S);
+  const bool writes_d = kt_lo == 0 && kt_lo < kt_hi;
 
   u32x4 kr[C::PER_T], vr[C::PER_T];
   auto load_tile = [&](int kt) {
@@ -537,8 +553,14 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
             const int j = kb + acc_row(r, h);
             p = ((CAUSAL & (j > qi)) | (j >= N)) ? 0.f : p;  // a select, not a branch
           }
-          dp[r] = p * (dp[r] - dl);
+          s[r] = p;
         }
+        if (kb == 0) {
+          const float dx = block_pdp_sum(s, dp, lane);
+          dl = d_from_block ? dx : dl;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl);
         // dQ^T += K^T dS^T: K^T through transpose reads of the key tile.
 #pragma unroll
         for (int t = 0; t < C::CPB; ++t) {
@@ -558,6 +580,10 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   int kt = kt_lo;
   for (; kt < min(kt_full, kt_hi); ++kt) tile(kt, BoolC<false>{});
   for (; kt < kt_hi; ++kt) tile(kt, BoolC<true>{});
+  if (writes_d && h == 0 && qi < N) {
+    Delta[sq.row0 + qi] = dl;
+    Lse2[sq.row0 + qi] = lse2;
+  }
 
   if (S > 1) {
     // One of S partial sums over the key tiles, scaled, as fp32 rows of
@@ -1262,12 +1288,13 @@ __global__ __launch_bounds__(256, dqpp::occupancy(D)) void bwd_dq_pp_kernel(cons
 #pragma unroll
     for (int c = 0; c < DCH; ++c) pc[c] = dot_chunk<T>(load16(O + off + c * 2 * CH), gf[c]);
   }
-  const float dl = row_dot<DCH>(pc, lane);  // D = rowsum(dO * O)
+  float dl = row_dot<DCH>(pc, lane);  // D = rowsum(dO * O)
   const float lse2 = LSE[sq.row0 + qc] * kLog2e;
-  if (h == 0 && qi < N) {
-    Delta[sq.row0 + qi] = dl;
-    Lse2[sq.row0 + qi] = lse2;
-  }
+  // Rows whose visible keys all lie in block 0 take D = sum_j P_ij dP_ij
+  // from that block instead (block_pdp_sum); only the first query tile
+  // (causal) or a sequence of at most 32 keys has such rows.
+  const bool d_from_block = (CAUSAL ? min(qi, N - 1) : N - 1) < KB;
+  const bool tile_has_block_d = CAUSAL ? q0 == 0 : N <= KB;
 #pragma unroll
   for (int b = 0; b < PF; ++b)
     if (b < nb) issue(b, b);
@@ -1304,22 +1331,37 @@ __global__ __launch_bounds__(256, dqpp::occupancy(D)) void bwd_dq_pp_kernel(cons
   // Block kb in slot SLOT: its products, dS^T = P^T (dP^T - D) and
   // dQ^T += K^T dS^T.  (The Q and dO rows and the dQ accumulators leave no
   // room for a second block's products in flight.)
-  auto block = [&](auto slotc, int kb, auto masked) {
+  // FIRST: block 0 of a tile with d_from_block rows (it is always masked).
+  auto block = [&](auto slotc, int kb, auto masked, auto first) {
     constexpr int SLOT = decltype(slotc)::value;
     constexpr bool MASKED = decltype(masked)::value;
+    constexpr bool FIRST = decltype(first)::value;
     const bool ahead = kb + PF < nb;
     if (ahead) issue(kb + PF, (SLOT + PF) % R);
     f32x16 s, dp;
     products(SLOT, s, dp);
     const int k0 = kb * KB;
+    if (FIRST) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
-      if (MASKED) {
-        const int j = k0 + acc_row(r, h);
-        p = ((CAUSAL & (j > qi)) | (j >= N)) ? 0.f : p;  // a select, not a branch
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+        const int j = acc_row(r, h);
+        s[r] = ((CAUSAL & (j > qi)) | (j >= N)) ? 0.f : p;
       }
-      dp[r] = p * (dp[r] - dl);
+      const float dx = block_pdp_sum(s, dp, lane);
+      dl = d_from_block ? dx : dl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+        if (MASKED) {
+          const int j = k0 + acc_row(r, h);
+          p = ((CAUSAL & (j > qi)) | (j >= N)) ? 0.f : p;  // a select, not a branch
+        }
+        dp[r] = p * (dp[r] - dl);
+      }
     }
     const char* kb_ = reinterpret_cast<const char*>(Ks[SLOT]);
     __builtin_amdgcn_sched_barrier(0);
@@ -1348,19 +1390,30 @@ __global__ __launch_bounds__(256, dqpp::occupancy(D)) void bwd_dq_pp_kernel(cons
   // mask; the diagonal and ragged blocks come last.
   const int nb_full = min(nb, CAUSAL ? min(q0, N) / KB : N / KB);
   int kb = 0;
+  // (A tile with d_from_block rows has at most one full block, so its block 0
+  // always runs in the loop below.)
   for (; kb + 4 <= nb_full; kb += 4) {
-    block(IntC<0>{}, kb, BoolC<false>{});
-    block(IntC<1>{}, kb + 1, BoolC<false>{});
-    block(IntC<2>{}, kb + 2, BoolC<false>{});
-    block(IntC<3>{}, kb + 3, BoolC<false>{});
+    block(IntC<0>{}, kb, BoolC<false>{}, BoolC<false>{});
+    block(IntC<1>{}, kb + 1, BoolC<false>{}, BoolC<false>{});
+    block(IntC<2>{}, kb + 2, BoolC<false>{}, BoolC<false>{});
+    block(IntC<3>{}, kb + 3, BoolC<false>{}, BoolC<false>{});
   }
   for (; kb < nb; ++kb) {
     switch (kb & 3) {
-      case 0: block(IntC<0>{}, kb, BoolC<true>{}); break;
-      case 1: block(IntC<1>{}, kb, BoolC<true>{}); break;
-      case 2: block(IntC<2>{}, kb, BoolC<true>{}); break;
-      default: block(IntC<3>{}, kb, BoolC<true>{}); break;
+      case 0:
+        if (kb == 0 && tile_has_block_d)
+          block(IntC<0>{}, kb, BoolC<true>{}, BoolC<true>{});
+        else
+          block(IntC<0>{}, kb, BoolC<true>{}, BoolC<false>{});
+        break;
+      case 1: block(IntC<1>{}, kb, BoolC<true>{}, BoolC<false>{}); break;
+      case 2: block(IntC<2>{}, kb, BoolC<true>{}, BoolC<false>{}); break;
+      default: block(IntC<3>{}, kb, BoolC<true>{}, BoolC<false>{}); break;
     }
+  }
+  if (h == 0 && qi < N) {
+    Delta[sq.row0 + qi] = dl;
+    Lse2[sq.row0 + qi] = lse2;
   }
 
   if (qi < N) {
@@ -1412,8 +1465,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const long long kv_rows = a.cu ? (long long)a.Hkv * a.T : (long long)BHkv * a.N;
   const float sl2 = a.scale * kLog2e;
   // Stage 1 is the dQ kernel, which also computes D and LSE * log2(e) for
-  // its rows; stage 3 has nothing left to do.
-  if (stage == 3) return hipSuccess;
+  // its rows; stage 2 the dK/dV kernel.
   if (stage == 1) {
     if constexpr (sizeof(T) == 2 && (D == 128 || D == 64)) {
       if (!force_generic_kernels()) {

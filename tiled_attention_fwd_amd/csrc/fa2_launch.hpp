@@ -185,7 +185,7 @@ inline bool force_generic_kernels() {
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_decode(const DecArgs& a);
 // stage 1: the dQ kernel, which also writes D = rowsum(dO * O) and
-// LSE * log2(e) to the workspace; 2: the dK/dV kernel; 3: nothing.
+// LSE * log2(e) to the workspace; 2: the dK/dV kernel.
 hipError_t launch_backward_stage(const BwdArgs& a, int stage);
 
 }  // namespace fa2

@@ -60,7 +60,9 @@ typedef enum {
   FA2_ERR_UNSUPPORTED = 2, /* d not in {16, 32, 64, 128}, or a pointer not
                               16-byte aligned                              */
   FA2_ERR_WORKSPACE = 3,   /* backward workspace NULL or too small         */
-  FA2_ERR_LAUNCH = 4       /* a HIP launch reported an error               */
+  FA2_ERR_LAUNCH = 4,      /* a HIP launch reported an error               */
+  FA2_ERR_SCRATCH = 5      /* fa2_backward_noalloc: the problem needs more
+                              workspace than its static buffer holds       */
 } fa2_status;
 
 /*
@@ -165,6 +167,36 @@ int fa2_backward_stage_ex(int stage, const void* q, const void* k, const void* v
                           const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
                           int H, int H_kv, int N, int d, float scale, int causal, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa2_backward_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels, results (the same bits as
+ * fa2_backward_ex) and errors, without the workspace arguments: the
+ * workspace is a static device array of FA2_NOALLOC_SCRATCH_BYTES bytes
+ * (64 MiB) inside the library, one per GPU, placed when the library's code
+ * object is loaded onto that GPU and held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call);
+ * on the first call on a device it looks up that device's copy with
+ * hipGetSymbolAddress.  The current device must be the one that `stream`
+ * and the tensors belong to.
+ *
+ * Limit: problems whose fa2_backward_workspace_size_ex exceeds
+ * FA2_NOALLOC_SCRATCH_BYTES are rejected with FA2_ERR_SCRATCH before any HIP
+ * call (D and LSE * log2(e) take 8 bytes per query row, so plain multi-head
+ * problems fit up to about 8 M rows B * H * N; split grouped-query and fp32
+ * walks add fp32 partial sums).  The buffer keeps the last call's contents;
+ * every call writes all it reads, so nothing needs clearing.  All calls on
+ * one GPU share the one buffer: calls whose work overlaps in time on that GPU
+ * (other streams, other threads) race and give wrong results; serialise them
+ * (one stream, or events between streams).
+ */
+#define FA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int fa2_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+                         void* stream);
 
 /*
  * Packed ragged batches (variable-length sequences).  The article's forward

@@ -31,7 +31,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert names == ["fa2_backward", "fa2_backward_ex", "fa2_backward_stage", "fa2_backward_stage_ex",
+    assert names == ["fa2_backward", "fa2_backward_ex", "fa2_backward_noalloc", "fa2_backward_stage",
+                     "fa2_backward_stage_ex",
                      "fa2_backward_stage_varlen", "fa2_backward_varlen", "fa2_backward_workspace_size",
                      "fa2_backward_workspace_size_ex", "fa2_backward_workspace_size_varlen", "fa2_decode",
                      "fa2_decode_workspace_size", "fa2_forward", "fa2_forward_ex", "fa2_forward_varlen",
@@ -303,3 +304,29 @@ def test_varlen_workspace(L):
     args = (A,) * 10 + (3, 4, 2, 1000, 600, 128, 0.125, 1, 1, A)
     assert L.fa2_backward_varlen(*args, need - 1, None) == fa.FA2_ERR_WORKSPACE
     assert L.fa2_backward_stage_varlen(4, *args, need, None) == fa.FA2_ERR_INVALID_ARG
+
+
+# fa2_backward_noalloc validates before any HIP call: bad arguments and
+# problems that need more than its static workspace are rejected on a host
+# without a GPU.
+def bwd_noalloc(L, B=1, H=2, H_kv=2, N=64, d=64, scale=0.125, dtype=1, ptr=A):
+    return L.fa2_backward_noalloc(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, B, H, H_kv, N, d, scale, 1, dtype,
+                                  None)
+
+
+def test_noalloc_rejects_problems_beyond_its_buffer(L):
+    # 64 x 64 x 4096 query rows: D and LSE*log2(e) alone take 128 MiB
+    assert fa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert L.fa2_backward_workspace_size_ex(64, 64, 64, 4096, 128, 1) > fa.NOALLOC_SCRATCH_BYTES
+    assert bwd_noalloc(L, B=64, H=64, H_kv=64, N=4096, d=128) == fa.FA2_ERR_SCRATCH
+    assert "static buffer" in fa.fa2_status_string(fa.FA2_ERR_SCRATCH)
+
+
+def test_noalloc_validates_like_backward(L):
+    assert bwd_noalloc(L, d=48) == fa.FA2_ERR_UNSUPPORTED
+    assert bwd_noalloc(L, H=4, H_kv=3) == fa.FA2_ERR_INVALID_ARG
+    assert bwd_noalloc(L, scale=float("nan")) == fa.FA2_ERR_INVALID_ARG
+    assert bwd_noalloc(L, dtype=7) == fa.FA2_ERR_INVALID_ARG
+    assert bwd_noalloc(L, ptr=None) == fa.FA2_ERR_INVALID_ARG
+    assert bwd_noalloc(L, ptr=A + 8) == fa.FA2_ERR_UNSUPPORTED
+    assert bwd_noalloc(L, B=0, ptr=None) == fa.FA2_OK

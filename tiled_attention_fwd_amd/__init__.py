@@ -9,6 +9,7 @@ Functions with the C names (``fa2_forward``, ``fa2_backward``,
 ``fa2_backward_stage``, their ``_ex`` forms with a key/value head count for
 grouped-query attention, ``fa2_backward_workspace_size`` (``_ex``),
 ``fa2_forward_varlen``, ``fa2_backward_varlen`` (packed ragged batches),
+``fa2_backward_noalloc`` (the backward with the library's static workspace),
 ``fa2_decode``, ``fa2_decode_workspace_size``, ``fa2_status_string``) take
 caller-allocated tensors like the C ABI; ``forward`` / ``backward`` /
 ``decode`` allocate the outputs (K and V may have fewer heads than Q: H_kv
@@ -30,6 +31,9 @@ FA2_ERR_INVALID_ARG = 1
 FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_WORKSPACE = 3
 FA2_ERR_LAUNCH = 4
+FA2_ERR_SCRATCH = 5
+# Bytes of the static workspace behind fa2_backward_noalloc (FA2_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
 
@@ -68,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.fa2_backward_workspace_size.restype = ctypes.c_size_t
         L.fa2_backward_workspace_size_ex.argtypes = [i, i, i, i, i, i]
         L.fa2_backward_workspace_size_ex.restype = ctypes.c_size_t
+        L.fa2_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa2_backward_noalloc.restype = i
         L.fa2_forward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         L.fa2_forward_varlen.restype = i
         L.fa2_backward_varlen.argtypes = [vp] * 10 + [i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
@@ -231,6 +237,27 @@ def fa2_backward_stage_ex(stage: int, q, k, v, o, dO, lse, dq, dk, dv, causal: b
     if workspace is None:
         raise ValueError("the stages share state through the workspace: pass one")
     _backward_call(True, int(stage), q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def fa2_backward_noalloc(q, k, v, o, dO, lse, dq, dk, dv, causal: bool = True, scale: float | None = None,
+                         stream=None) -> None:
+    """``fa2_backward_ex`` without a workspace argument: the library's static
+    per-GPU buffer serves as the workspace and nothing is allocated (for
+    callers that cannot allocate).  Problems needing more than
+    NOALLOC_SCRATCH_BYTES raise (FA2_ERR_SCRATCH); calls whose work overlaps
+    on one GPU share that buffer and race."""
+    _check_tensors(q, k, v, o, dO, lse, dq, dk, dv)
+    B, H, H_kv, N, d = _heads(q, k, v, o, dO, dq)
+    if dk.shape != k.shape or dv.shape != k.shape or dk.dtype != q.dtype or dv.dtype != q.dtype:
+        raise ValueError("dk, dv must have k's shape and q's dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    st = lib().fa2_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
+                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
+                                    _scale(scale, d), int(bool(causal)), _dtype_code(q.dtype),
+                                    _stream(stream, q.device))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_backward_noalloc")
 
 
 def _backward_call(ex, stage, q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream):

@@ -8,9 +8,41 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa2_launch.hpp"
 
+// Workspace of fa2_backward_noalloc: one copy per GPU, placed by the code
+// object loader and held until the process ends.  Host code never passes
+// this name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): it uses the device address that hipGetSymbolAddress returns for
+// the current device (scratch_base below).
+constexpr size_t kScratchBytes = FA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_base[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up with
+// hipGetSymbolAddress on the first call on that device and kept.
+hipError_t scratch_base(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_base[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_base[dev] = p;
+  }
+  *out = g_scratch_base[dev];
+  return hipSuccess;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -74,20 +106,35 @@ size_t ws_bytes(int B, int H, int H_kv, int N, int d, int dtype, long long rows,
   return fa2::ws_total_bytes((size_t)rows, d, dtype) + fa2::ws_part_bytes(kv_rows, d, S, rows, Sq);
 }
 
+// Checks of a backward call other than its workspace: FA2_OK, or the status
+// to report.  *empty is set for a problem with nothing to compute.
+int check_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int dtype,
+                   bool* empty) {
+  *empty = false;
+  int st = check_sizes(B, H, N, d, dtype);
+  if (st != FA2_OK) return st;
+  if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (is_empty(B, H, N)) {
+    *empty = true;
+    return FA2_OK;
+  }
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA2_ERR_UNSUPPORTED;
+  return FA2_OK;
+}
+
 // Stages stage_first .. stage_last of the backward; N as in forward_impl.
 int backward_impl(int stage_first, int stage_last, const void* q, const void* k, const void* v, const void* o,
                   const void* dO, const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N,
                   int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream,
                   const int* cu = nullptr, int T = 0) {
-  int st = check_sizes(B, H, N, d, dtype);
-  if (st != FA2_OK) return st;
-  if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
-  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
-  if (is_empty(B, H, N)) return FA2_OK;
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA2_ERR_UNSUPPORTED;
+  bool empty = false;
+  const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, dtype, &empty);
+  if (st != FA2_OK || empty) return st;
   const size_t rows = cu ? (size_t)H * T : (size_t)B * H * N;
   const long long kv_rows = cu ? (long long)H_kv * T : (long long)B * H_kv * N;
   if (!workspace || workspace_bytes < ws_bytes(B, H, H_kv, N, d, dtype, (long long)rows, kv_rows))
@@ -117,6 +164,8 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED: head dim not in {16,32,64,128} or pointer not 16-byte aligned";
     case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: backward workspace missing or too small";
     case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: a HIP kernel launch failed";
+    case FA2_ERR_SCRATCH:
+      return "FA2_ERR_SCRATCH: the problem needs more workspace than fa2_backward_noalloc's static buffer";
     default: return "unknown fa2 status";
   }
 }
@@ -168,6 +217,19 @@ int fa2_backward_ex(const void* q, const void* k, const void* v, const void* o, 
                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return backward_impl(1, 2, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, workspace,
                        workspace_bytes, stream);
+}
+
+int fa2_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+                         float scale, int causal, int dtype, void* stream) {
+  bool empty = false;
+  const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, dtype, &empty);
+  if (st != FA2_OK || empty) return st;
+  if (fa2_backward_workspace_size_ex(B, H, H_kv, N, d, dtype) > kScratchBytes) return FA2_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_base(&ws) != hipSuccess) return FA2_ERR_LAUNCH;
+  return backward_impl(1, 2, q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, ws,
+                       kScratchBytes, stream);
 }
 
 int fa2_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int Nmax,
     int BHkv, float sl2, float scale, int H, int G, const int* __restrict__ cu, int Ttot, int S,
-    float* __restrict__ PartK, float* __restrict__ PartV, long long kv_rows) {
+    float* __restrict__ PartK, float* __restrict__ PartV, long long kv_rows, int snake) {
   using C = DkdvTile<T, D>;
   constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB, QS = C::QS;
   // Double-buffered query-side tiles: one barrier per query tile.
@@ -164,7 +164,9 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
+  // Key tile kt = 0 is the heaviest (causal); see causal_rank.
+  const int kt = CAUSAL ? causal_rank(lin / (BHkv * S), (Nmax + DkdvTile<T, D>::BC - 1) / DkdvTile<T, D>::BC, snake != 0)
+                       : lin / (BHkv * S);
   const int sp = (lin % (BHkv * S)) / BHkv;  // which of the S pieces of the query-tile walk
   const int bhk = lin % BHkv;  // (sequence, key/value head); it serves query heads hk*G .. hk*G + G - 1
   const int bq = bhk / (H / G), hk = bhk % (H / G);
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
                                                         T* __restrict__ dQ, int Nmax,
                                                         int BH, int num_qt, float sl2, float scale, int H, int G,
                                                         const int* __restrict__ cu, int Ttot, int S,
-                                                        float* __restrict__ PartQ, long long rows) {
+                                                        float* __restrict__ PartQ, long long rows, int snake) {
   using C = DqTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int qt = CAUSAL ? (num_qt - 1 - lin / (BH * S)) : (lin / (BH * S));
+  const int qt = CAUSAL ? (num_qt - 1 - causal_rank(lin / (BH * S), num_qt, snake != 0)) : (lin / (BH * S));
   const int sp = (lin % (BH * S)) / BH;  // which of the S pieces of the key-tile walk
   const int bh = lin % BH;
   const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
@@ -1455,6 +1457,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __res
   store4<T>(Out + i, acc[0], acc[1], acc[2], acc[3]);
 }
 
+// Grids of at most this many workgroups (two per CU) take the snake order
+// of causal_rank.
+constexpr long long kSnakeGrid = 512;
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int BH = a.B * a.H;
@@ -1490,7 +1496,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), static_cast<const T*>(a.o), a.lse, a.lse2, a.delta,
-                       static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T, S, a.part, rows);
+                       static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T, S, a.part, rows,
+                       (int)(blocks * S <= kSnakeGrid));
     if (S > 1) {
       const long long n = rows * D;
       const unsigned rb = (unsigned)((n / 4 + 255) / 256);
@@ -1548,7 +1555,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
-                       a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T, S, part_k, part_v, kv_rows);
+                       a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T, S, part_k, part_v, kv_rows,
+                       (int)(blocks * S <= kSnakeGrid));
     if (S > 1) {
       const unsigned rb = (unsigned)((n / 4 + 255) / 256);
       hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,

@@ -273,6 +273,19 @@ __device__ __forceinline__ TileIdx xcd_head_major(int lin, int heads, int tiles)
   return TileIdx{s % tiles, (s / tiles) * 8 + x};
 }
 
+// Launch rank -> cost rank of a causal grid's tiles (cost rank 0 = the
+// heaviest tile).  A grid spanning many rounds of resident workgroups runs
+// heaviest first, so nothing long is left for the end.  A grid of at most two
+// workgroups per CU is placed in one go, its first half one per CU and its
+// second half beside it in the same CU order; there the second half is
+// reversed ("snake"), so each CU holds one heavy and one light tile instead
+// of two heavy ones or two light ones.
+__device__ __forceinline__ int causal_rank(int p, int n, bool snake) {
+  if (!snake) return p;
+  const int half = (n + 1) / 2;
+  return p < half ? p : n - 1 - (p - half);
+}
+
 struct SeqRows {
   long long row0;
   int n;

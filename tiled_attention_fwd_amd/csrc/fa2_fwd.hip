@@ -67,21 +67,32 @@ struct FwdTile {
   static constexpr int PER_T = (CHUNKS + 255) / 256;
 };
 
-template <typename T, int D, bool CAUSAL>
+// SPLIT = 1: four waves, each with its own 32 query rows, walk the key
+// tiles together.  SPLIT = 2 (fp32 grids too small to fill the device): the
+// 4 waves form 2 query groups of 32 rows, and the 2 waves of a group take
+// alternate key tiles (each step brings in one tile per wave), so the
+// longest walk is halved; at the end each pair merges its (max, sum, O) in
+// LDS with the same rescaling as the online softmax.
+template <typename T, int D, bool CAUSAL, int SPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int Nmax, int BH, int num_qt,
                                                      float sl2, int H, int G, const int* __restrict__ cu,
-                                                     int Ttot, int Nk) {
+                                                     int Ttot, int Nk, int snake) {
   using C = FwdTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) T Vs[2][BC * VS];
+  constexpr int BR = 32 * C::NW / SPLIT;  // query rows per workgroup
+  constexpr int CHUNKS = SPLIT * C::CHUNKS;
+  constexpr int PER_T = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) T Ks[2][SPLIT * BC * KS];
+  __shared__ __attribute__((aligned(16))) T Vs[2][SPLIT * BC * VS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
+  const int qg = w / SPLIT;  // query group of this wave
+  const int kp = w % SPLIT;  // which of each step's SPLIT key tiles it takes
   const int lin = blockIdx.x;
-  const int qt = CAUSAL ? (num_qt - 1 - lin / BH) : (lin / BH);
+  const int qt = CAUSAL ? (num_qt - 1 - causal_rank(lin / BH, num_qt, snake != 0)) : (lin / BH);
   const int bh = lin % BH;
   const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);
   const int N = sq.n;  // this sequence's length (query rows)
@@ -97,10 +108,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   const T* Qh = Q + base;
   const T* Kh = K + kv_base;
   const T* Vh = V + kv_base;
-  const int q0 = qt * C::BR;
-  if (q0 >= N) return;         // a tile past a shorter packed sequence
-  const int qw = q0 + 32 * w;  // first query row of this wave
-  const int qi = qw + l32;     // query row (column of S^T) owned by this lane
+  const int q0 = qt * BR;
+  if (q0 >= N) return;          // a tile past a shorter packed sequence
+  const int qw = q0 + 32 * qg;  // first query row of this wave
+  const int qi = qw + l32;      // query row (column of S^T) owned by this lane
 
   // Q^T as the B operand of S^T = K Q^T: lane holds its query row, chunked
   // over d.  Rows past N load row N-1 (finite) and are never stored.
@@ -111,31 +122,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
     for (int c = 0; c < C::DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
   }
 
-  const int kv_end = CAUSAL ? min(Nkv, q0 + C::BR + coff) : Nkv;
+  const int kv_end = CAUSAL ? min(Nkv, q0 + BR + coff) : Nkv;
   const int n_kt = (kv_end + BC - 1) / BC;
+  const int n_st = (n_kt + SPLIT - 1) / SPLIT;  // steps of SPLIT tiles
 
-  // Tile loads: rows past Nkv load row Nkv-1; those keys are masked to -inf, so
-  // their (finite) values never reach the output.
-  u32x4 kr[C::PER_T], vr[C::PER_T];
-  auto load_tile = [&](int kt) {
+  // Step loads: tiles SPLIT*st .. SPLIT*st + SPLIT - 1, rows past Nkv (and
+  // tiles past the last) load row Nkv-1; those keys are masked to -inf or
+  // never visited, so their (finite) values never reach the output.
+  u32x4 kr[PER_T], vr[PER_T];
+  auto load_step = [&](int st) {
 #pragma unroll
-    for (int u = 0; u < C::PER_T; ++u) {
+    for (int u = 0; u < PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::CHUNKS) {
-        const size_t off = (size_t)min(kt * BC + c / C::ROW_CH, Nkv - 1) * D + (c % C::ROW_CH) * CH;
+      if (c < CHUNKS) {
+        const int j = c / C::CHUNKS, cc = c % C::CHUNKS;
+        const size_t off = (size_t)min((SPLIT * st + j) * BC + cc / C::ROW_CH, Nkv - 1) * D + (cc % C::ROW_CH) * CH;
         kr[u] = load16(Kh + off);
         vr[u] = load16(Vh + off);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_step = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < C::PER_T; ++u) {
+    for (int u = 0; u < PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::CHUNKS) {
-        const int row = c / C::ROW_CH, col = (c % C::ROW_CH) * CH;
-        store16(&Ks[buf][row * KS + col], kr[u]);
-        store16(&Vs[buf][row * VS + col], vr[u]);
+      if (c < CHUNKS) {
+        const int j = c / C::CHUNKS, cc = c % C::CHUNKS;
+        const int row = cc / C::ROW_CH, col = (cc % C::ROW_CH) * CH;
+        store16(&Ks[buf][(j * BC + row) * KS + col], kr[u]);
+        store16(&Vs[buf][(j * BC + row) * VS + col], vr[u]);
       }
     }
   };
@@ -146,19 +161,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   float m_run = -INFINITY;  // running max of scaled logits, base-2 units
   float l_run = 0.f;        // this lane half's share of the running sum
 
-  load_tile(0);
-  store_tile(0);
+  load_step(0);
+  store_step(0);
   __syncthreads();
 
-  // One key tile.  Each 32-key block runs its own online-softmax update, so
-  // a block's exponentials depend only on its own scores and the next
-  // block's score MFMAs can run under them.
-  auto tile = [&](int kt, auto masked) {
+  // One key tile of this wave.  Each 32-key block runs its own
+  // online-softmax update, so a block's exponentials depend only on its own
+  // scores and the next block's score MFMAs can run under them.
+  auto tile = [&](int kt, const T* ks, const T* vs, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    const bool more = kt + 1 < n_kt;
-    if (more) load_tile(kt + 1);
-    const T* ks = Ks[kt & 1];
-    const T* vs = Vs[kt & 1];
     const int kb0 = kt * BC;
     // 32-key blocks of this tile that hold a key this wave may see.
     const int last_key = CAUSAL ? min(qw + 31 + coff, Nkv - 1) : Nkv - 1;
@@ -219,15 +230,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
         }
       }
     }
-    if (more) store_tile((kt + 1) & 1);
-    __syncthreads();
   };
   // Key tiles wholly below every row of this query tile and wholly before Nkv
   // need no mask; the diagonal and ragged tiles come last.
   const int kt_full = min(n_kt, CAUSAL ? min(q0 + coff, Nkv) / BC : Nkv / BC);
-  int kt = 0;
-  for (; kt < kt_full; ++kt) tile(kt, BoolC<false>{});
-  for (; kt < n_kt; ++kt) tile(kt, BoolC<true>{});
+  if constexpr (SPLIT == 1) {
+    auto step = [&](int kt, auto masked) {
+      const bool more = kt + 1 < n_kt;
+      if (more) load_step(kt + 1);
+      tile(kt, Ks[kt & 1], Vs[kt & 1], masked);
+      if (more) store_step((kt + 1) & 1);
+      __syncthreads();
+    };
+    int kt = 0;
+    for (; kt < kt_full; ++kt) step(kt, BoolC<false>{});
+    for (; kt < n_kt; ++kt) step(kt, BoolC<true>{});
+  } else {
+    for (int st = 0; st < n_st; ++st) {
+      const bool more = st + 1 < n_st;
+      if (more) load_step(st + 1);
+      const int kt = SPLIT * st + kp;  // this wave's tile (uniform per wave)
+      const T* ks = &Ks[st & 1][kp * BC * KS];
+      const T* vs = &Vs[st & 1][kp * BC * VS];
+      if (kt < kt_full)
+        tile(kt, ks, vs, BoolC<false>{});
+      else if (kt < n_kt)
+        tile(kt, ks, vs, BoolC<true>{});
+      if (more) store_step((st + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (SPLIT == 2) {
+    // Merge the two walks of each query group: the odd wave leaves its max,
+    // sums and accumulators in LDS (the tiles are no longer read: the last
+    // step ended with a barrier), the even one combines them.  The even wave
+    // walked key 0, so its max is finite.
+    constexpr int SLOT = C::NB * 16 * 64 + 2 * 64;  // floats per query group
+    static_assert(2 * SLOT * sizeof(float) <= sizeof(Ks), "merge area");
+    float* xo = reinterpret_cast<float*>(&Ks[0][0]) + qg * SLOT;
+    if (kp == 1) {
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(16 * b + r) * 64 + lane] = o[b][r];
+      xo[C::NB * 16 * 64 + lane] = m_run;
+      xo[C::NB * 16 * 64 + 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kp == 1) return;
+    const float m1 = xo[C::NB * 16 * 64 + lane];
+    const float l1 = xo[C::NB * 16 * 64 + 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[b][r] = o[b][r] * a0 + xo[(16 * b + r) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
+  }
 
   const float l_tot = l_run + swap_halves(l_run, lane);
   if (qi < N) {
@@ -480,6 +543,11 @@ __global__ __launch_bounds__(256, fpp::occupancy(D)) void fwd_pp_kernel(const T*
 }
 
 
+// Grids of at most this many workgroups (two per CU) are placed in one go:
+// they take the snake order of causal_rank, and fp32 ones below it split
+// their walks.
+constexpr long long kFwdSplitGrid = 512;
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   if constexpr (sizeof(T) == 2 && (D == 128 || D == 64)) {
@@ -498,13 +566,28 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   }
   using C = FwdTile<T, D>;
   const int BH = a.B * a.H;
-  const int num_qt = (a.N + C::BR - 1) / C::BR;
-  const long long blocks = (long long)num_qt * BH;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+  const long long blocks4 = (long long)((a.N + C::BR - 1) / C::BR) * BH;
+  if constexpr (sizeof(T) == 4 && D <= 64) {
+    // fp32 grids of fewer than two 128-row tiles per CU: split each walk
+    // over two waves (half-size query tiles, so twice the workgroups).
+    if (a.Nk == 0 && blocks4 < kFwdSplitGrid) {
+      const int num_qt = (a.N + C::BR / 2 - 1) / (C::BR / 2);
+      const long long blocks = (long long)num_qt * BH;
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, 2>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T, a.Nk,
+                         (int)(blocks <= kFwdSplitGrid));
+      return hipGetLastError();
+    }
+  }
+  const int num_qt = (a.N + C::BR - 1) / C::BR;
+  const long long blocks = blocks4;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, 1>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T, a.Nk);
+                     static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T, a.Nk,
+                     (int)(blocks <= kFwdSplitGrid));
   return hipGetLastError();
 }
 

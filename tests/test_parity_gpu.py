@@ -411,7 +411,7 @@ def test_decode_split_and_unsplit_agree(d, dtype, monkeypatch):
     assert rel_err(a[1].cpu(), b[1].cpu()) <= TOL[dtype]
 
 
-# fa2_backward_stage 1, 2, 3 in order is fa2_backward, whichever kernels the
+# fa2_backward_stage 1 then 2 is fa2_backward, whichever kernels the
 # stages enqueue: the ring or the generic dQ kernel with D as stage 1, the
 # d = 128, d = 64 or generic dK/dV kernel, the split grouped dK/dV with its
 # partial sum (grouped-query at d = 128), the fp32 split query walk.

@@ -40,7 +40,7 @@
 //                    them; in fp32, a 1/S share of the query tiles), and
 //                    bwd_dkdv_reduce_kernel sums the S fp32 partials in a
 //                    fixed order.
-//   Stage 3 enqueues nothing (dQ came with stage 1).
+//   There is no third stage: dQ comes with stage 1.
 // Every kernel takes its (sequence, head) rows from seq_rows, so fixed-length
 // and packed ragged batches share them.
 // The two halves recompute S and dP instead of exchanging dS, so dQ needs no

@@ -190,6 +190,19 @@ def test_short_rows_many_seeds(N, dtype):
     assert max(errs) <= TOL[dtype]
 
 
+# Causal grids with 256 or more (sequence, key/value head) pairs visit a
+# head's tiles together on one XCD instead of running the heaviest tiles of
+# all heads first.  Whole tensors against the oracle (outputs NaN-prefilled,
+# so a tile the order skipped shows up): the ring forward and dQ kernels at
+# d = 128 and 64, the d = 128 and d = 64 dK/dV kernels, grouped-query heads
+# whose split dK/dV grid also takes the order, and a ragged length.
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype", [(64, 4, 4, 257, 128, "bf16"), (32, 8, 8, 300, 64, "bf16"),
+                                                (64, 8, 4, 200, 128, "bf16"), (32, 8, 8, 129, 128, "f16")])
+def test_head_grouped_causal_order(B, H, H_kv, N, d, dtype):
+    w = workloads.custom(B, H, N, d, dtype, True, 6100 + B + H + H_kv + N + d, name="many_heads", H_kv=H_kv)
+    run_case(w)
+
+
 def test_large_logits_causal_bf16():
     """x8 Q and K (logit sigma near 64 nats) with the causal mask and a
     ragged length: repeated max rescaling along the diagonal."""

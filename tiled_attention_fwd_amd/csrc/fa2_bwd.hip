@@ -143,7 +143,7 @@ struct DkdvTile {
   static constexpr int ROW_CH = D / CH;
   static constexpr int Q_CHUNKS = BR * ROW_CH;
   static constexpr int Q_PER_T = (Q_CHUNKS + 255) / 256;
-  static constexpr int OCC = (sizeof(T) == 2 && D <= 64) ? 2 : 1;  // workgroups per CU the registers allow
+  static constexpr int OCC = (D <= 64) ? 2 : 1;  // workgroups per CU the registers allow
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -255,6 +255,16 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     dp = f32x16{};
     const T* qrow = qs + (32 * mb + l32) * QS + h * CH;
     const T* grow = gs + (32 * mb + l32) * QS + h * CH;
+    if constexpr (sizeof(T) == 4) {
+      // fp32: an MFMA chunk is four 64-cycle products, so fragments read
+      // one chunk ahead hide the LDS latency and keep the registers for a
+      // second wave per SIMD.
+#pragma unroll
+      for (int c = 0; c < C::DCH; ++c) {
+        mfma_chunk<T>(s, load16(qrow + c * 2 * CH), kf[c]);
+        mfma_chunk<T>(dp, load16(grow + c * 2 * CH), vf[c]);
+      }
+    } else {
     // All operand fragments first, so the wave waits on LDS once per phase.
     u32x4 qa[C::DCH], ga[C::DCH];
 #pragma unroll
@@ -266,6 +276,7 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     for (int c = 0; c < C::DCH; ++c) {
       mfma_chunk<T>(s, qa[c], kf[c]);
       mfma_chunk<T>(dp, ga[c], vf[c]);
+    }
     }
   };
   auto grad = [&](const float* ls, const float* ds, int i0, int mb, f32x16& s, f32x16& dp, auto masked) {
@@ -665,9 +676,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_d128_kernel(const T* __restri
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
-  const int sp = (lin % (BHkv * S)) / BHkv;  // which 1/S of the group's query heads
-  const int bhk = lin % BHkv;  // (sequence, key/value head)
+  // Key tiles ascending: for causal the heaviest go first (causal_order
+  // over the S * BHkv (piece, sequence, key/value head) triples).
+  const CausalOrder co = CAUSAL ? causal_order(lin, BHkv * S, (Nmax + d128::BC - 1) / d128::BC, BHkv * S >= kHeadGroupedHeads)
+                                : CausalOrder{lin / (BHkv * S), lin % (BHkv * S)};
+  const int kt = co.rank;
+  const int sp = co.head / BHkv;  // which 1/S of the group's query heads
+  const int bhk = co.head % BHkv;  // (sequence, key/value head)
   const int gpw = G / S;       // query heads walked by this workgroup: h0 .. h0 + gpw - 1
   const int bq = bhk / (H / G), hk = bhk % (H / G);
   const int h0 = hk * G + sp * gpw;
@@ -939,9 +954,13 @@ __global__ __launch_bounds__(256, CAUSAL ? 2 : 3) void bwd_dkdv_d64_kernel(const
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  const int kt = lin / (BHkv * S);  // ascending: for causal the heaviest key tiles go first
-  const int sp = (lin % (BHkv * S)) / BHkv;  // which 1/S of the group's query heads
-  const int bhk = lin % BHkv;  // (sequence, key/value head)
+  // Key tiles ascending: for causal the heaviest go first (causal_order
+  // over the S * BHkv (piece, sequence, key/value head) triples).
+  const CausalOrder co = CAUSAL ? causal_order(lin, BHkv * S, (Nmax + d64::BC - 1) / d64::BC, BHkv * S >= kHeadGroupedHeads)
+                                : CausalOrder{lin / (BHkv * S), lin % (BHkv * S)};
+  const int kt = co.rank;
+  const int sp = co.head / BHkv;  // which 1/S of the group's query heads
+  const int bhk = co.head % BHkv;  // (sequence, key/value head)
   const int gpw = G / S;       // query heads walked by this workgroup: h0 .. h0 + gpw - 1
   const int bq = bhk / (H / G), hk = bhk % (H / G);
   const int h0 = hk * G + sp * gpw;
@@ -1217,9 +1236,15 @@ __global__ __launch_bounds__(256, dqpp::occupancy(D)) void bwd_dq_pp_kernel(cons
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  // Causal: heaviest query tiles first, heads fastest; otherwise a head's
+  // Causal: heaviest query tiles first (causal_order); otherwise a head's
   // tiles together on one XCD.
-  const TileIdx ti = CAUSAL ? TileIdx{num_qt - 1 - lin / BH, lin % BH} : xcd_head_major(lin, BH, num_qt);
+  TileIdx ti;
+  if (CAUSAL) {
+    const CausalOrder co = causal_order(lin, BH, num_qt, BH / G >= kHeadGroupedHeads);
+    ti = TileIdx{num_qt - 1 - co.rank, co.head};
+  } else {
+    ti = xcd_head_major(lin, BH, num_qt);
+  }
   const int qt = ti.tile;
   const int bh = ti.head;
   const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);

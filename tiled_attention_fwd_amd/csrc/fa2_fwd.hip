@@ -357,9 +357,15 @@ __global__ __launch_bounds__(256, fpp::occupancy(D)) void fwd_pp_kernel(const T*
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int lin = blockIdx.x;
-  // Causal: heaviest query tiles first, heads fastest; otherwise a head's
+  // Causal: heaviest query tiles first (causal_order); otherwise a head's
   // tiles together on one XCD.
-  const TileIdx ti = CAUSAL ? TileIdx{num_qt - 1 - lin / BH, lin % BH} : xcd_head_major(lin, BH, num_qt);
+  TileIdx ti;
+  if (CAUSAL) {
+    const CausalOrder co = causal_order(lin, BH, num_qt, BH / G >= kHeadGroupedHeads);
+    ti = TileIdx{num_qt - 1 - co.rank, co.head};
+  } else {
+    ti = xcd_head_major(lin, BH, num_qt);
+  }
   const int qt = ti.tile;
   const int bh = ti.head;
   const SeqRows sq = seq_rows(cu, Nmax, Ttot, bh / H, bh % H, H);

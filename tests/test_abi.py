@@ -132,18 +132,26 @@ def test_workspace_size_ex_formula(L):
     # keeps 4 query tiles (32 rows at d >= 64, 64 below) per piece:
     # 32 key tiles x 4 x 2 = 256 -> S = 2
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 0) == plain + 2 * al(2 * B * 2 * N * d * 4)
-    # the 8x8x512x64 shape: 4 key tiles x 64 = 256 -> S = 2 (walks of 16 query tiles)
-    assert L.fa2_backward_workspace_size(8, 8, 512, 64, 0) == 2 * al(64 * 512 * 4) + 2 * al(2 * 64 * 512 * 64 * 4)
-    # 4x4x256x32: a walk of 4 query tiles is not split
+    # fp32 at d <= 64 with fewer than 512 unsplit workgroups and N >= 256
+    # first pairs the walks inside each workgroup (64 keys or 64 query rows
+    # per workgroup, no partial sums), then splits what is left while every
+    # wave keeps 4 query steps (dK/dV) or 8 key tiles (dQ) per piece.
+    # The 8x8x512x64 shape: 8 key tiles x 64 = 512 paired workgroups, no split
+    assert L.fa2_backward_workspace_size(8, 8, 512, 64, 0) == 2 * al(64 * 512 * 4)
+    # 4x4x256x32: paired, walks of 4 query steps / 8 key tiles: no split
     assert L.fa2_backward_workspace_size(4, 4, 256, 32, 0) == 2 * al(16 * 256 * 4)
     # 2048 workgroups already: no split
     assert L.fa2_backward_workspace_size_ex(8, 16, 16, 2048, d, 0) == 2 * al(8 * 16 * 2048 * 4)
-    # fp32 dQ splits each query tile's walk over 32-key tiles the same way (8
-    # key tiles per piece at least) into the same area: 1x2x2048x64 has 32
-    # query tiles -> dQ S = 7, dK/dV S = 16 (64-tile walks); the larger of
-    # the two partial sets sizes the area
+    # 1x2x2048x64, paired: 32 x 2 = 64 workgroups each side; dK/dV walks of
+    # 64 query steps -> S = 8 (512 workgroups, 64 / 8 >= 8), dQ walks of 64
+    # key tiles -> S = 4 (64 / 4 >= 16); the larger of the two partial sets
+    # sizes the area
     assert L.fa2_backward_workspace_size(1, 2, 2048, 64, 0) == \
-        2 * al(2 * 2048 * 4) + max(2 * al(16 * 2 * 2048 * 64 * 4), al(7 * 2 * 2048 * 64 * 4))
+        2 * al(2 * 2048 * 4) + max(2 * al(8 * 2 * 2048 * 64 * 4), al(4 * 2 * 2048 * 64 * 4))
+    # the unpaired rule still holds at d = 128 and below N = 256: 1x2x2048x128
+    # dK/dV 16 query tiles x 2 = 32 -> S = 16, dQ S = 7
+    assert L.fa2_backward_workspace_size(1, 2, 2048, 128, 0) == \
+        2 * al(2 * 2048 * 4) + max(2 * al(16 * 2 * 2048 * 128 * 4), al(7 * 2 * 2048 * 128 * 4))
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, d, 2) == plain + 2 * al(4 * B * 2 * N * d * 4)
     assert L.fa2_backward_workspace_size_ex(B, H, 2, N, 64, 1) == plain
     assert L.fa2_backward_workspace_size_ex(B, H, 3, N, d, 1) == 0

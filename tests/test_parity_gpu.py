@@ -452,14 +452,19 @@ def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
         assert torch.equal(a, b), "%s: staged backward differs from fa2_backward" % name
 
 
-# fp32 with few heads and long walks: the dK/dV stage cuts each key tile's
-# walk over the query tiles, and the dQ kernel each query tile's walk over
-# the key tiles, into pieces whose fp32 partial sums a second kernel adds
-# (1x2x2048x64: 16 and 7 pieces; a ragged non-causal length and grouped
-# heads as well).
-@pytest.mark.parametrize("B,H,H_kv,N,causal", [(1, 2, 2, 2048, True), (1, 2, 2, 1500, False), (1, 4, 2, 1200, True)])
-def test_fp32_split_walks(B, H, H_kv, N, causal):
-    w = workloads.custom(B, H, N, 64, "f32", causal, 7300 + N + H_kv, name="f32split", H_kv=H_kv)
+# fp32 with few heads and long walks: at d <= 64 the two waves of each key
+# (query) group first take alternate query steps (key tiles) and add their
+# accumulators in LDS; then the dK/dV stage cuts each key tile's walk over
+# the query tiles, and the dQ kernel each query tile's walk over the key
+# tiles, into pieces whose fp32 partial sums a second kernel adds
+# (1x2x2048x64: paired, then 8 and 4 pieces; at d = 128 unpaired, 16 and 7
+# pieces; d = 32 pairs steps of 64 query rows; a ragged non-causal length
+# and grouped heads as well).
+@pytest.mark.parametrize("B,H,H_kv,N,d,causal", [(1, 2, 2, 2048, 64, True), (1, 2, 2, 1500, 64, False),
+                                                 (1, 4, 2, 1200, 64, True), (1, 2, 2, 2048, 128, True),
+                                                 (2, 2, 2, 700, 32, True), (2, 3, 1, 333, 16, False)])
+def test_fp32_split_walks(B, H, H_kv, N, d, causal):
+    w = workloads.custom(B, H, N, d, "f32", causal, 7300 + N + H_kv + d, name="f32split", H_kv=H_kv)
     run_case(w)
 
 

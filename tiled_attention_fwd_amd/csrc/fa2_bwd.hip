@@ -146,27 +146,36 @@ struct DkdvTile {
   static constexpr int OCC = (D <= 64) ? 2 : 1;  // workgroups per CU the registers allow
 };
 
-template <typename T, int D, bool CAUSAL>
+// QP = 2 (fp32 grids too small to fill the device): the workgroup's 4 waves
+// form 2 key groups of 32 keys (64 keys per workgroup), and the 2 waves of a
+// group take alternate query steps (each iteration brings in two steps, one
+// per wave), so the longest walk is halved without partial sums in memory;
+// at the end the second wave of each group hands its dK, dV accumulators to
+// the first through LDS.
+template <typename T, int D, bool CAUSAL, int QP>
 __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, T* __restrict__ dK, T* __restrict__ dV, int Nmax,
     int BHkv, float sl2, float scale, int H, int G, const int* __restrict__ cu, int Ttot, int S,
     float* __restrict__ PartK, float* __restrict__ PartV, long long kv_rows, int snake) {
   using C = DkdvTile<T, D>;
-  constexpr int CH = C::CH, BR = C::BR, BC = C::BC, MB = C::MB, QS = C::QS;
-  // Double-buffered query-side tiles: one barrier per query tile.
-  __shared__ __attribute__((aligned(16))) T Qs[2][BR * QS];
-  __shared__ __attribute__((aligned(16))) T dOs[2][BR * QS];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BR];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][BR];
+  constexpr int CH = C::CH, BR = C::BR, MB = C::MB, QS = C::QS;
+  constexpr int BC = C::BC / QP;  // keys per workgroup
+  // Double-buffered query-side tiles (QP query steps each): one barrier per
+  // iteration.
+  __shared__ __attribute__((aligned(16))) T Qs[2][QP * BR * QS];
+  __shared__ __attribute__((aligned(16))) T dOs[2][QP * BR * QS];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][QP * BR];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][QP * BR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
+  const int kg = w % (C::NW / QP);  // key group (32 keys) of this wave
+  const int qp = w / (C::NW / QP);  // which query step of each iteration it takes
   const int lin = blockIdx.x;
   // Key tile kt = 0 is the heaviest (causal); see causal_rank.
-  const int kt = CAUSAL ? causal_rank(lin / (BHkv * S), (Nmax + DkdvTile<T, D>::BC - 1) / DkdvTile<T, D>::BC, snake != 0)
-                       : lin / (BHkv * S);
+  const int kt = CAUSAL ? causal_rank(lin / (BHkv * S), (Nmax + BC - 1) / BC, snake != 0) : lin / (BHkv * S);
   const int sp = (lin % (BHkv * S)) / BHkv;  // which of the S pieces of the query-tile walk
   const int bhk = lin % BHkv;  // (sequence, key/value head); it serves query heads hk*G .. hk*G + G - 1
   const int bq = bhk / (H / G), hk = bhk % (H / G);
@@ -180,8 +189,8 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   const float* dlh = Delta;
   const int kv0 = kt * BC;
   if (kv0 >= N) return;  // a tile past a shorter packed sequence
-  const int kw = kv0 + 32 * w;  // first key of this wave
-  const int kj = kw + l32;      // key (accumulator column) owned by this lane
+  const int kw = kv0 + 32 * kg;  // first key of this wave
+  const int kj = kw + l32;       // key (accumulator column) owned by this lane
 
   // K and V rows of this lane as B operands of S = Q K^T and dP = dO V^T
   // (rows past N load row N-1; their weights are masked to 0).
@@ -208,19 +217,22 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   const int qt_begin = qt_first + (int)((long long)(n_qt - qt_first) * sp / S);
   const int qt_end = qt_first + (int)((long long)(n_qt - qt_first) * (sp + 1) / S);
 
-  u32x4 qr[C::Q_PER_T], gr[C::Q_PER_T];
+  // The rows of QP consecutive query steps starting at step qt.
+  constexpr int Q_CHUNKS = QP * C::Q_CHUNKS;
+  constexpr int Q_PER_T = (Q_CHUNKS + 255) / 256;
+  u32x4 qr[Q_PER_T], gr[Q_PER_T];
   float lr = 0.f, dr = 0.f;
   auto load_q = [&](int qt) {
 #pragma unroll
-    for (int u = 0; u < C::Q_PER_T; ++u) {
+    for (int u = 0; u < Q_PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::Q_CHUNKS) {
+      if (c < Q_CHUNKS) {
         const size_t off = (size_t)min(qt * BR + c / C::ROW_CH, N - 1) * D + (c % C::ROW_CH) * CH;
         qr[u] = load16(Qh + off);
         gr[u] = load16(dOh + off);
       }
     }
-    if (tid < BR) {
+    if (tid < QP * BR) {
       const int i = qt * BR + tid;
       lr = i < N ? lseh[i] * kLog2e : INFINITY;  // rows past N get P = 0
       dr = i < N ? dlh[i] : 0.f;
@@ -228,15 +240,15 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
   };
   auto store_q = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < C::Q_PER_T; ++u) {
+    for (int u = 0; u < Q_PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::Q_CHUNKS) {
+      if (c < Q_CHUNKS) {
         const int row = c / C::ROW_CH, col = (c % C::ROW_CH) * CH;
         store16(&Qs[buf][row * QS + col], qr[u]);
         store16(&dOs[buf][row * QS + col], gr[u]);
       }
     }
-    if (tid < BR) {
+    if (tid < QP * BR) {
       lse_s[buf][tid] = lr;
       dl_s[buf][tid] = dr;
     }
@@ -315,16 +327,22 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     }
   };
 
-  auto iteration = [&](int qt, int it, auto masked) {
+  // Iteration it: query steps qt0 .. qt0 + QP - 1 in the buffers, this
+  // wave's step qt = qt0 + qp.
+  auto iteration = [&](int it, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     const int buf = it & 1;
-    const T* qs = Qs[buf];
-    const T* gs = dOs[buf];
-    const float* ls = lse_s[buf];
-    const float* ds = dl_s[buf];
+    const int qt0 = qt_begin + QP * it;
+    const int qt = qt0 + qp;
+    const T* qs = Qs[buf] + qp * BR * QS;
+    const T* gs = dOs[buf] + qp * BR * QS;
+    const float* ls = lse_s[buf] + qp * BR;
+    const float* ds = dl_s[buf] + qp * BR;
     const int i0 = qt * BR;
 
-    if (MASKED || MB != 2 || sizeof(T) != 2) {
+    if (QP > 1 && qt >= qt_end) {
+      // (the last iteration of an odd walk: this wave has no step)
+    } else if (MASKED || MB != 2 || sizeof(T) != 2) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int ib = i0 + 32 * mb;
@@ -347,9 +365,9 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
       grad(ls, ds, i0, 1, s1, dp1, BoolC<false>{});
       mm_kv(qs, gs, 1, s1, dp1);
     }
-    if (qt + 1 < qt_end) store_q(buf ^ 1);
+    if (qt0 + QP < qt_end) store_q(buf ^ 1);
     __syncthreads();
-    if (qt + 2 < qt_end) load_q(qt + 2);
+    if (qt0 + 2 * QP < qt_end) load_q(qt0 + 2 * QP);
   };
   // Query tiles that cross this key tile's diagonal band (or every tile when
   // the key tile is ragged) run with the mask; the rest need none.  The walk
@@ -365,12 +383,49 @@ __global__ __launch_bounds__(256, (DkdvTile<T, D>::OCC)) void bwd_dkdv_kernel(
     if (qt_begin < qt_end) {
       load_q(qt_begin);
       store_q(0);
-      if (qt_begin + 1 < qt_end) load_q(qt_begin + 1);
+      if (qt_begin + QP < qt_end) load_q(qt_begin + QP);
     }
     __syncthreads();
-    int qt = qt_begin, it = 0;
-    for (; qt < min(qt_mask_end, qt_end); ++qt, ++it) iteration(qt, it, BoolC<true>{});
-    for (; qt < qt_end; ++qt, ++it) iteration(qt, it, BoolC<false>{});
+    if constexpr (QP == 1) {
+      int qt = qt_begin, it = 0;
+      for (; qt < min(qt_mask_end, qt_end); ++qt, ++it) iteration(it, BoolC<true>{});
+      for (; qt < qt_end; ++qt, ++it) iteration(it, BoolC<false>{});
+    } else {
+      const int n_it = (qt_end - qt_begin + QP - 1) / QP;
+      for (int it = 0; it < n_it; ++it) {
+        if (qt_begin + QP * it + qp < qt_mask_end)  // uniform per wave
+          iteration(it, BoolC<true>{});
+        else
+          iteration(it, BoolC<false>{});
+      }
+    }
+  }
+
+  if constexpr (QP > 1) {
+    // The second wave of each key group leaves its accumulators in LDS (the
+    // query tiles are no longer read), the first adds them to its own.
+    constexpr int SLOT = 2 * C::NB * 16 * 64;  // floats per wave
+    static_assert((C::NW / QP) * SLOT * sizeof(float) <= sizeof(Qs), "merge area");
+    float* xm = reinterpret_cast<float*>(&Qs[0][0]) + kg * SLOT;
+    __syncthreads();
+    if (qp == 1) {
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xm[(16 * b + r) * 64 + lane] = dk[b][r];
+          xm[(16 * (C::NB + b) + r) * 64 + lane] = dv[b][r];
+        }
+    }
+    __syncthreads();
+    if (qp == 1) return;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[b][r] += xm[(16 * b + r) * 64 + lane];
+        dv[b][r] += xm[(16 * (C::NB + b) + r) * 64 + lane];
+      }
   }
 
   if (S > 1) {
@@ -441,7 +496,13 @@ struct DqTile {
   static constexpr int OCC = (sizeof(T) == 4 && D == 128) ? 1 : 2;  // workgroups per CU
 };
 
-template <typename T, int D, bool CAUSAL>
+// KP = 2 (fp32 grids too small to fill the device): the 4 waves form 2 row
+// groups of 32 query rows (64 rows per workgroup), and the 2 waves of a
+// group take alternate key tiles (each step brings in two tiles, one per
+// wave), so the longest walk is halved without partial sums in memory; at
+// the end the second wave of each group hands its dQ accumulators to the
+// first through LDS.
+template <typename T, int D, bool CAUSAL, int KP>
 __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ dO,
                                                         const T* __restrict__ O, const float* __restrict__ LSE,
@@ -452,12 +513,15 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
                                                         float* __restrict__ PartQ, long long rows, int snake) {
   using C = DqTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) T Vs[2][BC * VS];
+  constexpr int BR = C::BR / KP;  // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) T Ks[2][KP * BC * KS];
+  __shared__ __attribute__((aligned(16))) T Vs[2][KP * BC * VS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
+  const int qg = w % (C::NW / KP);  // row group (32 query rows) of this wave
+  const int kp = w / (C::NW / KP);  // which key tile of each step it takes
   const int lin = blockIdx.x;
   const int qt = CAUSAL ? (num_qt - 1 - causal_rank(lin / (BH * S), num_qt, snake != 0)) : (lin / (BH * S));
   const int sp = (lin % (BH * S)) / BH;  // which of the S pieces of the key-tile walk
@@ -468,9 +532,9 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   const size_t kv_base = (size_t)seq_rows(cu, Nmax, Ttot, bh / H, (bh % H) / G, H / G).row0 * D;
   const T* Kh = K + kv_base;
   const T* Vh = V + kv_base;
-  const int q0 = qt * C::BR;
+  const int q0 = qt * BR;
   if (q0 >= N) return;  // a tile past a shorter packed sequence
-  const int qw = q0 + 32 * w;  // first query row of this wave
+  const int qw = q0 + 32 * qg;  // first query row of this wave
   const int qi = qw + l32;     // query row (column of S^T) owned by this lane
 
   // Q and dO rows of this lane (B operands); its LSE (base 2) and D, which
@@ -496,20 +560,24 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   // from that first 32-key block instead (block_pdp_sum).
   const bool d_from_block = (CAUSAL ? min(qi, N - 1) : N - 1) < 32;
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int n_kt = (kv_end + BC - 1) / BC;
   // This workgroup's piece of the walk: key tiles [kt_lo, kt_hi).  The one
-  // piece that walks key tile 0 writes D and LSE * log2(e) of these rows.
+  // piece that walks key tile 0 writes D and LSE * log2(e) of these rows
+  // (with KP = 2, the wave of each pair that takes tile 0).
   const int kt_lo = (int)((long long)n_kt * sp / S);
   const int kt_hi = (int)((long long)n_kt * (sp + 1) / S);
-  const bool writes_d = kt_lo == 0 && kt_lo < kt_hi;
+  const bool writes_d = kt_lo == 0 && kt_lo < kt_hi && kp == 0;
 
-  u32x4 kr[C::PER_T], vr[C::PER_T];
+  // The key and value rows of KP consecutive key tiles starting at tile kt.
+  constexpr int CHUNKS = KP * C::CHUNKS;
+  constexpr int PER_T = (CHUNKS + 255) / 256;
+  u32x4 kr[PER_T], vr[PER_T];
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < C::PER_T; ++u) {
+    for (int u = 0; u < PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::CHUNKS) {
+      if (c < CHUNKS) {
         const size_t off = (size_t)min(kt * BC + c / C::ROW_CH, N - 1) * D + (c % C::ROW_CH) * CH;
         kr[u] = load16(Kh + off);
         vr[u] = load16(Vh + off);
@@ -518,9 +586,9 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < C::PER_T; ++u) {
+    for (int u = 0; u < PER_T; ++u) {
       const int c = tid + 256 * u;
-      if (c < C::CHUNKS) {
+      if (c < CHUNKS) {
         const int row = c / C::ROW_CH, col = (c % C::ROW_CH) * CH;
         store16(&Ks[buf][row * KS + col], kr[u]);
         store16(&Vs[buf][row * VS + col], vr[u]);
@@ -538,15 +606,20 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
   }
   __syncthreads();
 
-  auto tile = [&](int kt, auto masked) {
+  // Step st: key tiles kt0 .. kt0 + KP - 1 in the buffers, this wave's tile
+  // kt = kt0 + kp (none past kt_hi).
+  auto tile = [&](int st, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    const bool more = kt + 1 < kt_hi;
-    if (more) load_tile(kt + 1);
-    const T* ks = Ks[(kt - kt_lo) & 1];
-    const T* vs = Vs[(kt - kt_lo) & 1];
+    const int kt0 = kt_lo + KP * st;
+    const int kt = kt0 + kp;
+    const bool more = kt0 + KP < kt_hi;
+    if (more) load_tile(kt0 + KP);
+    const T* ks = Ks[st & 1] + kp * BC * KS;
+    const T* vs = Vs[st & 1] + kp * BC * VS;
     const int kb0 = kt * BC;
     const int last_key = CAUSAL ? min(qw + 31, N - 1) : N - 1;
-    const int nlive = MASKED ? (last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1)) : C::NJB;
+    const int nlive = (KP > 1 && kt >= kt_hi) ? 0
+                      : MASKED ? (last_key < kb0 ? 0 : min(C::NJB, (last_key - kb0) / 32 + 1)) : C::NJB;
 #pragma unroll
     for (int jb = 0; jb < C::NJB; ++jb) {
       if (jb < nlive) {
@@ -584,15 +657,43 @@ __global__ __launch_bounds__(256, (DqTile<T, D>::OCC)) void bwd_dq_kernel(const 
         }
       }
     }
-    if (more) store_tile((kt + 1 - kt_lo) & 1);
+    if (more) store_tile((st + 1) & 1);
     __syncthreads();
   };
   // Key tiles wholly below every row of this query tile and wholly before N
   // need no mask; the diagonal and ragged tiles come last.
   const int kt_full = min(n_kt, CAUSAL ? min(q0, N) / BC : N / BC);
-  int kt = kt_lo;
-  for (; kt < min(kt_full, kt_hi); ++kt) tile(kt, BoolC<false>{});
-  for (; kt < kt_hi; ++kt) tile(kt, BoolC<true>{});
+  if constexpr (KP == 1) {
+    int kt = kt_lo;
+    for (; kt < min(kt_full, kt_hi); ++kt) tile(kt - kt_lo, BoolC<false>{});
+    for (; kt < kt_hi; ++kt) tile(kt - kt_lo, BoolC<true>{});
+  } else {
+    const int n_st = (kt_hi - kt_lo + KP - 1) / KP;
+    for (int st = 0; st < n_st; ++st) {
+      if (kt_lo + KP * st + kp < kt_full)  // uniform per wave
+        tile(st, BoolC<false>{});
+      else
+        tile(st, BoolC<true>{});
+    }
+    // The second wave of each row group leaves its accumulators in LDS (the
+    // tiles are no longer read), the first adds them to its own.
+    constexpr int SLOT = C::NB * 16 * 64;  // floats per wave
+    static_assert((C::NW / KP) * SLOT * sizeof(float) <= sizeof(Ks), "merge area");
+    float* xm = reinterpret_cast<float*>(&Ks[0][0]) + qg * SLOT;
+    __syncthreads();
+    if (kp == 1) {
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xm[(16 * b + r) * 64 + lane] = dq[b][r];
+    }
+    __syncthreads();
+    if (kp == 1) return;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[b][r] += xm[(16 * b + r) * 64 + lane];
+  }
   if (writes_d && h == 0 && qi < N) {
     Delta[sq.row0 + qi] = dl;
     Lse2[sq.row0 + qi] = lse2;
@@ -1512,17 +1613,28 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
       }
     }
     using C = DqTile<T, D>;
-    // fp32 splits each query tile's key walk (a.dq_splits pieces).
+    // fp32 splits each query tile's key walk (a.dq_splits pieces, after the
+    // paired walks of small grids).
     const int S = sizeof(T) == 4 ? a.dq_splits : 1;
-    const int num_qt = (a.N + C::BR - 1) / C::BR;
+    constexpr bool can_pair = sizeof(T) == 4 && D <= 64;
+    const bool paired = can_pair && fp32_paired_walks(a.B, a.H, a.N, D, a.dtype);
+    const int br = paired ? C::BR / 2 : C::BR;
+    const int num_qt = (a.N + br - 1) / br;
     const long long blocks = (long long)num_qt * BH;
     if (blocks * S > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const long long rows = a.cu ? (long long)a.H * a.T : (long long)BH * a.N;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dO), static_cast<const T*>(a.o), a.lse, a.lse2, a.delta,
-                       static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T, S, a.part, rows,
-                       (int)(blocks * S <= kSnakeGrid));
+    if (paired)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, can_pair ? 2 : 1>), dim3((unsigned)(blocks * S)), dim3(256), 0,
+                         a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                         static_cast<const T*>(a.v), static_cast<const T*>(a.dO), static_cast<const T*>(a.o), a.lse,
+                         a.lse2, a.delta, static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T, S,
+                         a.part, rows, (int)(blocks * S <= kSnakeGrid));
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, 1>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         static_cast<const T*>(a.dO), static_cast<const T*>(a.o), a.lse, a.lse2, a.delta,
+                         static_cast<T*>(a.dq), a.N, BH, num_qt, sl2, a.scale, a.H, G, a.cu, a.T, S, a.part, rows,
+                         (int)(blocks * S <= kSnakeGrid));
     if (S > 1) {
       const long long n = rows * D;
       const unsigned rb = (unsigned)((n / 4 + 255) / 256);
@@ -1569,19 +1681,30 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   }
   if (stage == 2) {
     using C = DkdvTile<T, D>;
-    // fp32 splits each key tile's query walk (a.splits pieces); the 16-bit
-    // types walk it whole here (their splits are the d = 128 kernel's).
+    // fp32 splits each key tile's query walk (a.splits pieces, after the
+    // paired walks of small grids); the 16-bit types walk it whole here
+    // (their splits are the d = 128 kernel's).
     const int S = sizeof(T) == 4 ? a.splits : 1;
-    const long long blocks = (long long)((a.N + C::BC - 1) / C::BC) * BHkv;
+    constexpr bool can_pair = sizeof(T) == 4 && D <= 64;
+    const bool paired = can_pair && fp32_paired_walks(a.B, a.Hkv, a.N, D, a.dtype);
+    const int bc = paired ? C::BC / 2 : C::BC;
+    const long long blocks = (long long)((a.N + bc - 1) / bc) * BHkv;
     if (blocks * S > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const long long n = kv_rows * D;  // elements of dK (and of dV)
     float* part_k = a.part;
     float* part_v = a.part + align256((size_t)S * n * sizeof(float)) / sizeof(float);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
-                       a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T, S, part_k, part_v, kv_rows,
-                       (int)(blocks * S <= kSnakeGrid));
+    if (paired)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, can_pair ? 2 : 1>), dim3((unsigned)(blocks * S)), dim3(256),
+                         0, a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                         static_cast<const T*>(a.v), static_cast<const T*>(a.dO), a.lse, a.delta,
+                         static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T, S,
+                         part_k, part_v, kv_rows, (int)(blocks * S <= kSnakeGrid));
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, 1>), dim3((unsigned)(blocks * S)), dim3(256), 0, a.stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         static_cast<const T*>(a.dO), a.lse, a.delta, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                         a.N, BHkv, sl2, a.scale, a.H, G, a.cu, a.T, S, part_k, part_v, kv_rows,
+                         (int)(blocks * S <= kSnakeGrid));
     if (S > 1) {
       const unsigned rb = (unsigned)((n / 4 + 255) / 256);
       hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T>), dim3(rb, 2), dim3(256), 0, a.stream, part_k, part_v,

@@ -85,13 +85,27 @@ inline size_t ws_total_bytes(size_t rows, int /*d*/, int /*dtype*/) { return 2 *
 // consecutive pieces (as long as the longest walk keeps at least 4 query
 // tiles per piece), and the same second kernel sums the pieces' partials.
 // With causal masking this also shortens the heaviest workgroup's walk.
+//
+// At d <= 64 a small fp32 grid first halves the walks inside each workgroup
+// (fp32_paired_walks): the dK/dV workgroup covers 64 keys and its two waves
+// per key group take alternate query steps, the dQ workgroup covers 64 rows
+// and its two waves per row group take alternate key tiles, each pair adding
+// its accumulators in LDS at the end.  That doubles the grid with no partial
+// sums in memory; the S pieces above are then cut from what is left.  (A
+// walk of fewer than 256 keys or queries has too few steps to share.)
+inline bool fp32_paired_walks(int B, int heads, int N, int d, int dtype) {
+  return dtype == kF32 && d <= 64 && N >= 256 && (long long)((N + 127) / 128) * B * heads < 512;
+}
 inline int dkdv_splits(int B, int Hkv, int G, int N, int d, int dtype) {
   if (dtype == kF32) {
     const int br = d >= 64 ? 32 : 64;  // query rows per step of the fp32 generic kernel
     const int steps = (N + br - 1) / br;
-    const long long base = (long long)((N + 127) / 128) * B * Hkv;
+    const bool paired = fp32_paired_walks(B, Hkv, N, d, dtype);
+    const int bc = paired ? 64 : 128;    // keys per workgroup
+    const int per = paired ? 8 : 4;      // query steps a piece keeps at least
+    const long long base = (long long)((N + bc - 1) / bc) * B * Hkv;
     int S = 1;
-    while (base * S < 512 && steps / (S + 1) >= 4) ++S;
+    while (base * S < 512 && steps / (S + 1) >= per) ++S;
     return S;
   }
   if (G <= 1 || d != 128) return 1;
@@ -111,9 +125,12 @@ inline int dkdv_splits(int B, int Hkv, int G, int N, int d, int dtype) {
 inline int dq_splits(int B, int H, int N, int d, int dtype) {
   if (dtype != kF32) return 1;
   const int steps = (N + 31) / 32;
-  const long long base = (long long)((N + 127) / 128) * B * H;
+  const bool paired = fp32_paired_walks(B, H, N, d, dtype);
+  const int br = paired ? 64 : 128;    // query rows per workgroup
+  const int per = paired ? 16 : 8;     // key tiles a piece keeps at least
+  const long long base = (long long)((N + br - 1) / br) * B * H;
   int S = 1;
-  while (base * S < 512 && steps / (S + 1) >= 8) ++S;
+  while (base * S < 512 && steps / (S + 1) >= per) ++S;
   return S;
 }
 // kv_rows: rows of dK ([B, Hkv, N] or, packed, [Hkv, T]); rows: rows of dQ.

@@ -55,7 +55,7 @@ typedef enum { FA2_F32 = 0, FA2_BF16 = 1, FA2_F16 = 2 } fa2_dtype;
 typedef enum {
   FA2_OK = 0,
   FA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, scale not finite
-                              or not > 0, dtype not an fa2_dtype, size
+                              or zero, dtype not an fa2_dtype, size
                               overflow (N * d must stay below 2^31)        */
   FA2_ERR_UNSUPPORTED = 2, /* d not in {16, 32, 64, 128}, or a pointer not
                               16-byte aligned                              */
@@ -74,7 +74,11 @@ typedef enum {
  * rounded to nearest even (the backward likewise rounds dS).  The article
  * names half-precision floats as a source of rounding error to watch
  * (section "Numerical Stability and Loss Drift"); FA2_F16 is that type.
- * scale: the factor on q . k (commonly 1/sqrt(d)); must be finite and > 0.
+ * scale: the factor on q . k (commonly 1/sqrt(d)); must be finite and
+ * nonzero.  A negative factor is computed as |scale| * (-q) . k (the query
+ * fragments' sign bits flipped in registers, exact in every type).  Zero is
+ * rejected: the kernels fold the factor into the exponent of every logit,
+ * and a masked logit (-inf) times zero is not a number.
  * causal: nonzero keeps keys j <= i (top-left aligned).
  */
 int fa2_forward(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -64,7 +64,7 @@ def test_forward_null_pointer(L, arg):
     (dict(N=-3), fa.FA2_ERR_INVALID_ARG), (dict(d=0), fa.FA2_ERR_INVALID_ARG),
     (dict(d=48), fa.FA2_ERR_UNSUPPORTED), (dict(d=256), fa.FA2_ERR_UNSUPPORTED),
     (dict(dtype=3), fa.FA2_ERR_INVALID_ARG), (dict(dtype=-1), fa.FA2_ERR_INVALID_ARG),
-    (dict(scale=0.0), fa.FA2_ERR_INVALID_ARG), (dict(scale=-0.5), fa.FA2_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA2_ERR_INVALID_ARG), (dict(scale=-0.0), fa.FA2_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA2_ERR_INVALID_ARG), (dict(scale=float("inf")), fa.FA2_ERR_INVALID_ARG),
     (dict(q=MIS), fa.FA2_ERR_UNSUPPORTED), (dict(lse=MIS), fa.FA2_ERR_UNSUPPORTED),
     (dict(N=1 << 24, d=128), fa.FA2_ERR_INVALID_ARG),

@@ -36,12 +36,14 @@ def gpu_decode(q, k, v, causal, scale):
     return o.t, lse.t
 
 
-def run_decode_case(w, heads=None):
+def run_decode_case(w, heads=None, scale=None):
     """heads: (b, key/value head) pairs to compare (with their query heads);
-    None compares everything."""
-    log("decode case: %s seed=%d" % (w.describe(), w.seed))
+    None compares everything.  scale: the factor on q . k (default: the
+    workload's)."""
+    scale = w.scale if scale is None else scale
+    log("decode case: %s seed=%d scale=%g" % (w.describe(), w.seed, scale))
     q, k, v = workloads.make_decode_inputs(w, device="cuda")
-    o, lse = gpu_decode(q, k, v, w.causal, w.scale)
+    o, lse = gpu_decode(q, k, v, w.causal, scale)
     o, lse = o.float().cpu(), lse.cpu()
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     G = w.H // w.H_kv
@@ -49,7 +51,7 @@ def run_decode_case(w, heads=None):
         [(slice(b, b + 1), slice(h * G, (h + 1) * G), slice(h, h + 1)) for b, h in heads]
     eo = el = 0.0
     for bs, hs, ks in sel:
-        o_r, lse_r = oracle.decode(qc[bs, hs], kc[bs, ks], vc[bs, ks], w.scale, w.causal)
+        o_r, lse_r = oracle.decode(qc[bs, hs], kc[bs, ks], vc[bs, ks], scale, w.causal)
         eo = max(eo, rel_err(o[bs, hs], o_r))
         el = max(el, rel_err(lse[bs, hs], lse_r))
     log("  errors: O=%.3g LSE=%.3g" % (eo, el))
@@ -115,6 +117,19 @@ GENERIC_CASES = [
 def test_decode_parity_generic(B, H, H_kv, Nq, Nk, d, dtype, causal):
     seed = 4300 + 7 * B + 13 * H + H_kv + 31 * Nq + Nk + d + (1 if causal else 0)
     run_decode_case(workloads.DecodeWorkload("decode", B, H, H_kv, Nq, Nk, d, dtype, causal, seed))
+
+
+# A negative factor on q . k: the split-cache kernel (d = 128 and 64) and the
+# generic forward kernel decoding run it as |scale| * (-q) . k.
+@pytest.mark.parametrize("B,H,H_kv,Nq,Nk,d,dtype,causal", [
+    (2, 8, 2, 4, 1000, 128, "bf16", True),
+    (1, 6, 3, 5, 300, 64, "f16", True),
+    (2, 2, 1, 3, 129, 32, "f32", True),
+])
+def test_decode_negative_scale(B, H, H_kv, Nq, Nk, d, dtype, causal):
+    seed = 4400 + 7 * B + 13 * H + H_kv + 31 * Nq + Nk + d
+    run_decode_case(workloads.DecodeWorkload("decode", B, H, H_kv, Nq, Nk, d, dtype, causal, seed),
+                    scale=-0.9 / d ** 0.5)
 
 
 def test_decode_workload_sampled_heads():

@@ -16,6 +16,7 @@ whose guard bands are checked afterwards (an out-of-bounds write at a ragged
 tail changes them).
 """
 import json
+import math
 import os
 import sys
 
@@ -79,11 +80,13 @@ def gpu_fwd_bwd(q, k, v, dO, causal, scale):
     return o.t, lse.t, dq.t, dk.t, dv.t
 
 
-def check_against_oracle(w, q, k, v, dO, outs, heads=None):
+def check_against_oracle(w, q, k, v, dO, outs, heads=None, scale=None):
     """Compare GPU outputs with the oracle, on all heads or on (b, h) pairs.
 
     With grouped-query inputs h names a key/value head, and the comparison
-    covers it together with every query head of its group."""
+    covers it together with every query head of its group.  scale: the factor
+    on q . k (default: the workload's, 1/sqrt(d))."""
+    scale = w.scale if scale is None else scale
     o, lse, dq, dk, dv = (t.float().cpu() for t in outs)
     qc, kc, vc, gc = (t.cpu() for t in (q, k, v, dO))
     G = q.shape[1] // k.shape[1]
@@ -93,8 +96,8 @@ def check_against_oracle(w, q, k, v, dO, outs, heads=None):
         sel = [(slice(b, b + 1), slice(h * G, (h + 1) * G), slice(h, h + 1)) for b, h in heads]
     errs = {n: 0.0 for n in ("O", "LSE", "dQ", "dK", "dV")}
     for bs, hs, ks in sel:
-        o_r, lse_r = oracle.fwd(qc[bs, hs], kc[bs, ks], vc[bs, ks], w.scale, w.causal)
-        dq_r, dk_r, dv_r = oracle.bwd(qc[bs, hs], kc[bs, ks], vc[bs, ks], gc[bs, hs], w.scale, w.causal)
+        o_r, lse_r = oracle.fwd(qc[bs, hs], kc[bs, ks], vc[bs, ks], scale, w.causal)
+        dq_r, dk_r, dv_r = oracle.bwd(qc[bs, hs], kc[bs, ks], vc[bs, ks], gc[bs, hs], scale, w.causal)
         errs["O"] = max(errs["O"], rel_err(o[bs, hs], o_r))
         errs["LSE"] = max(errs["LSE"], rel_err(lse[bs, hs], lse_r))
         errs["dQ"] = max(errs["dQ"], rel_err(dq[bs, hs], dq_r))
@@ -103,11 +106,12 @@ def check_against_oracle(w, q, k, v, dO, outs, heads=None):
     return errs
 
 
-def run_case(w, heads=None):
-    log("case: %s seed=%d" % (w.describe(), w.seed))
+def run_case(w, heads=None, scale=None):
+    scale = w.scale if scale is None else scale
+    log("case: %s seed=%d scale=%g" % (w.describe(), w.seed, scale))
     q, k, v, dO = workloads.make_inputs(w, device="cuda")
-    outs = gpu_fwd_bwd(q, k, v, dO, w.causal, w.scale)
-    errs = check_against_oracle(w, q, k, v, dO, outs, heads)
+    outs = gpu_fwd_bwd(q, k, v, dO, w.causal, scale)
+    errs = check_against_oracle(w, q, k, v, dO, outs, heads, scale)
     log("  errors: " + " ".join("%s=%.3g" % kv for kv in errs.items()))
     record = os.environ.get("FA2_PARITY_RECORD")
     if record:  # one JSON line per compared case, for the measurement notes
@@ -466,6 +470,24 @@ def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
 def test_fp32_split_walks(B, H, H_kv, N, d, causal):
     w = workloads.custom(B, H, N, d, "f32", causal, 7300 + N + H_kv + d, name="f32split", H_kv=H_kv)
     run_case(w)
+
+
+# A negative factor on q . k is valid: the forward runs it as
+# |scale| * (-q) . k (the sign bits of its query fragments flipped), the
+# backward as given.  One case per kernel family: the d = 128 and d = 64
+# ring kernels (grouped and not), fp16, the fp32 generic kernels with split
+# walks, the 16-bit generic kernels at d = 32 and d = 16.
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", [
+    (1, 4, 4, 300, 128, "bf16", True),
+    (2, 4, 2, 257, 64, "bf16", False),
+    (1, 2, 2, 200, 128, "f16", True),
+    (2, 4, 4, 520, 64, "f32", True),
+    (1, 3, 3, 130, 32, "bf16", True),
+    (1, 2, 1, 77, 16, "f32", False),
+])
+def test_negative_scale(B, H, H_kv, N, d, dtype, causal):
+    w = workloads.custom(B, H, N, d, dtype, causal, 900 + N + d, H_kv=H_kv)
+    run_case(w, scale=-1.3 / math.sqrt(d))
 
 
 def test_internal_workspace_on_a_side_stream():

@@ -19,25 +19,27 @@ from tests.test_parity_gpu import TOL, Guarded, log, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def gpu_varlen(w, q, k, v, dO, cu):
+def gpu_varlen(w, q, k, v, dO, cu, scale):
     H, T, d = q.shape
     o = Guarded(q.shape, q.dtype)
     lse = Guarded((H, T), torch.float32)
-    fa.fa2_forward_varlen(q, k, v, o.t, lse.t, cu, w.max_seqlen, w.causal, w.scale)
+    fa.fa2_forward_varlen(q, k, v, o.t, lse.t, cu, w.max_seqlen, w.causal, scale)
     dq = Guarded(q.shape, q.dtype)
     dk, dv = Guarded(k.shape, q.dtype), Guarded(k.shape, q.dtype)
-    fa.fa2_backward_varlen(q, k, v, o.t, dO, lse.t, dq.t, dk.t, dv.t, cu, w.max_seqlen, w.causal, w.scale)
+    fa.fa2_backward_varlen(q, k, v, o.t, dO, lse.t, dq.t, dk.t, dv.t, cu, w.max_seqlen, w.causal, scale)
     torch.cuda.synchronize()
     for g, name in ((o, "O"), (lse, "LSE"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):
         assert g.guards_intact(), "%s: write outside the output tensor" % name
     return o.t, lse.t, dq.t, dk.t, dv.t
 
 
-def run_varlen_case(w, seqs=None):
-    """seqs: indices of the sequences to compare (None: all)."""
-    log("varlen case: %s seed=%d lengths=%s" % (w.describe(), w.seed, list(w.lengths)))
+def run_varlen_case(w, seqs=None, scale=None):
+    """seqs: indices of the sequences to compare (None: all); scale: the
+    factor on q . k (default: the workload's)."""
+    scale = w.scale if scale is None else scale
+    log("varlen case: %s seed=%d lengths=%s scale=%g" % (w.describe(), w.seed, list(w.lengths), scale))
     q, k, v, dO, cu = workloads.make_varlen_inputs(w, device="cuda")
-    outs = gpu_varlen(w, q, k, v, dO, cu)
+    outs = gpu_varlen(w, q, k, v, dO, cu, scale)
     o, lse, dq, dk, dv = (t.float().cpu() for t in outs)
     qc, kc, vc, gc = (t.cpu() for t in (q, k, v, dO))
     offs = w.cu_seqlens()
@@ -47,8 +49,8 @@ def run_varlen_case(w, seqs=None):
         if e == s:
             continue
         sl = lambda t: t[:, s:e].unsqueeze(0)  # noqa: E731  [1, heads, n, d]
-        o_r, lse_r = oracle.fwd(sl(qc), sl(kc), sl(vc), w.scale, w.causal)
-        dq_r, dk_r, dv_r = oracle.bwd(sl(qc), sl(kc), sl(vc), sl(gc), w.scale, w.causal)
+        o_r, lse_r = oracle.fwd(sl(qc), sl(kc), sl(vc), scale, w.causal)
+        dq_r, dk_r, dv_r = oracle.bwd(sl(qc), sl(kc), sl(vc), sl(gc), scale, w.causal)
         for name, a, r in (("O", sl(o), o_r), ("LSE", lse[:, s:e].unsqueeze(0), lse_r), ("dQ", sl(dq), dq_r),
                            ("dK", sl(dk), dk_r), ("dV", sl(dv), dv_r)):
             errs[name] = max(errs[name], rel_err(a, r))
@@ -94,6 +96,17 @@ VARLEN_CASES = [
 def test_varlen_parity(lengths, H, H_kv, d, dtype, causal):
     seed = 5000 + sum(lengths) % 997 + 7 * H + H_kv + d + (1 if causal else 0)
     run_varlen_case(vw(lengths, H, H_kv, d, dtype, causal, seed))
+
+
+@pytest.mark.parametrize("lengths,H,H_kv,d,dtype,causal", [
+    ([300, 1, 129], 2, 2, 128, "bf16", True),
+    ([513, 31], 6, 3, 64, "f16", True),
+    ([700, 65], 2, 1, 64, "f32", False),
+])
+def test_varlen_negative_scale(lengths, H, H_kv, d, dtype, causal):
+    """A negative factor on q . k through the packed entry points."""
+    seed = 5300 + sum(lengths) % 997 + 7 * H + H_kv + d
+    run_varlen_case(vw(lengths, H, H_kv, d, dtype, causal, seed), scale=-1.1 / d ** 0.5)
 
 
 def test_varlen_rows_past_the_last_sequence_untouched():

@@ -88,7 +88,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
-  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale == 0.f) return FA2_ERR_INVALID_ARG;
   if (is_empty(B, H, N)) return FA2_OK;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -115,7 +115,7 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
   int st = check_sizes(B, H, N, d, dtype);
   if (st != FA2_OK) return st;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
-  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale == 0.f) return FA2_ERR_INVALID_ARG;
   if (is_empty(B, H, N)) {
     *empty = true;
     return FA2_OK;
@@ -283,7 +283,7 @@ int fa2_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0 || d <= 0) return FA2_ERR_INVALID_ARG;
   if (dtype != FA2_F32 && dtype != FA2_BF16 && dtype != FA2_F16) return FA2_ERR_INVALID_ARG;
   if (!valid_hkv(H, H_kv)) return FA2_ERR_INVALID_ARG;
-  if (!isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale == 0.f) return FA2_ERR_INVALID_ARG;
   if ((int64_t)N_k * d >= ((int64_t)1 << 31) || (int64_t)N_q * d >= ((int64_t)1 << 31))
     return FA2_ERR_INVALID_ARG;
   if ((int64_t)B * H * N_q >= ((int64_t)1 << 31)) return FA2_ERR_INVALID_ARG;

@@ -113,6 +113,23 @@ __device__ __forceinline__ void mfma_chunk<float>(f32x16& acc, u32x4 a, u32x4 b)
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], acc, 0, 0, 0);
 }
 
+// A negative scale: scale * q.k = |scale| * (-q).k.  The kernels that keep
+// a running maximum of raw scores (forward, decoding) scale that maximum by
+// the factor, which is only the maximum of the scaled scores for a factor
+// >= 0; so with a negative factor they flip the sign bits of their query
+// fragments once (exact in every type) and work with |factor|.
+template <typename T>
+__device__ __forceinline__ void negate_fragments_if(u32x4* f, int n, float& sl2) {
+  if (sl2 < 0.f) {
+    constexpr unsigned kSign = sizeof(T) == 4 ? 0x80000000u : 0x80008000u;
+#pragma unroll
+    for (int c = 0; c < n; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[c][e] ^= kSign;
+    sl2 = -sl2;
+  }
+}
+
 // Pack accumulator registers CH*t .. CH*t+CH-1 into one B-operand fragment
 // (bf16, fp16: round to nearest even, two per dword).
 template <typename T>

@@ -149,6 +149,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const T* __restrict__ Q, con
 #pragma unroll
     for (int c = 0; c < DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
   }
+  negate_fragments_if<T>(qf, DCH, sl2);
 #pragma unroll
   for (int t = 0; t < PF; ++t)
     if (t < nb) issue(kb0 + t, t);

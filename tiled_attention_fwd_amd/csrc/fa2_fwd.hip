@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
 #pragma unroll
     for (int c = 0; c < C::DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
   }
+  negate_fragments_if<T>(qf, C::DCH, sl2);
 
   const int kv_end = CAUSAL ? min(Nkv, q0 + BR + coff) : Nkv;
   const int n_kt = (kv_end + BC - 1) / BC;
@@ -428,6 +429,7 @@ __global__ __launch_bounds__(256, fpp::occupancy(D)) void fwd_pp_kernel(const T*
 #pragma unroll
     for (int c = 0; c < DCH; ++c) qf[c] = load16(qrow + c * 2 * CH);
   }
+  negate_fragments_if<T>(qf, DCH, sl2);
 #pragma unroll
   for (int b = 0; b < PF; ++b)
     if (b < nb) issue(b, b);

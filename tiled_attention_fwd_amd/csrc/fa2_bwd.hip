@@ -18,11 +18,15 @@
 //                    dP^T = V dO^T on MFMA, so each lane owns one query and
 //                    its LSE and D are scalars, then dQ^T += K^T dS^T.  It
 //                    first computes D = rowsum(dO o O) (it holds the lane's
-//                    dO row already and loads its O row) and LSE * log2(e)
-//                    for its rows and writes both to the workspace for the
-//                    dK/dV kernel.  For the 16-bit types at d = 128 and 64,
-//                    bwd_dq_pp_kernel runs the same pass over a ring of
-//                    direct-loaded 32-key blocks, like fwd_pp_kernel.
+//                    dO row already and loads its O row; a row whose keys
+//                    all lie in its first 32-key block takes sum_j P_ij dP_ij
+//                    from that block instead) and LSE * log2(e) for its rows
+//                    and writes both to the workspace for the dK/dV kernel.
+//                    For the 16-bit types at d = 128 and 64, bwd_dq_pp_kernel
+//                    runs the same pass over a ring of direct-loaded 32-key
+//                    blocks, like fwd_pp_kernel.  Small fp32 grids pair the
+//                    walks: 64-row workgroups whose two waves per row group
+//                    take alternate key tiles and add their dQ in LDS.
 //   bwd_dkdv_kernel  stage 2: one workgroup per (batch, head, 128-key tile);
 //                    each of its 4 waves owns 32 keys and keeps K, V (as MFMA
 //                    B operands) and its dK^T, dV^T accumulators in registers
@@ -39,7 +43,9 @@
 //                    head of its key/value head's group (or a 1/S share of
 //                    them; in fp32, a 1/S share of the query tiles), and
 //                    bwd_dkdv_reduce_kernel sums the S fp32 partials in a
-//                    fixed order.
+//                    fixed order.  Small fp32 grids first pair the walks:
+//                    64-key workgroups whose two waves per key group take
+//                    alternate query steps and add dK, dV in LDS.
 //   There is no third stage: dQ comes with stage 1.
 // Every kernel takes its (sequence, head) rows from seq_rows, so fixed-length
 // and packed ragged batches share them.

@@ -463,10 +463,13 @@ def test_stages_equal_full_backward(dtype, H, H_kv, d, causal):
 # tiles, into pieces whose fp32 partial sums a second kernel adds
 # (1x2x2048x64: paired, then 8 and 4 pieces; at d = 128 unpaired, 16 and 7
 # pieces; d = 32 pairs steps of 64 query rows; a ragged non-causal length
-# and grouped heads as well).
+# and grouped heads as well).  The forward of these grids splits its key
+# walks too: over two waves at d = 64, over four at d <= 32 (the last two
+# cases: up to 47 key tiles of a 32-row query tile, four walks merged).
 @pytest.mark.parametrize("B,H,H_kv,N,d,causal", [(1, 2, 2, 2048, 64, True), (1, 2, 2, 1500, 64, False),
                                                  (1, 4, 2, 1200, 64, True), (1, 2, 2, 2048, 128, True),
-                                                 (2, 2, 2, 700, 32, True), (2, 3, 1, 333, 16, False)])
+                                                 (2, 2, 2, 700, 32, True), (2, 3, 1, 333, 16, False),
+                                                 (1, 4, 4, 1500, 32, True), (2, 2, 1, 1025, 16, False)])
 def test_fp32_split_walks(B, H, H_kv, N, d, causal):
     w = workloads.custom(B, H, N, d, "f32", causal, 7300 + N + H_kv + d, name="f32split", H_kv=H_kv)
     run_case(w)

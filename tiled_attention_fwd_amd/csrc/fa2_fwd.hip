@@ -72,7 +72,11 @@ struct FwdTile {
 // 4 waves form 2 query groups of 32 rows, and the 2 waves of a group take
 // alternate key tiles (each step brings in one tile per wave), so the
 // longest walk is halved; at the end each pair merges its (max, sum, O) in
-// LDS with the same rescaling as the online softmax.
+// LDS with the same rescaling as the online softmax.  SPLIT = 4 (the same
+// grids at d <= 32): one query group of 32 rows whose 4 waves take every
+// fourth key tile, with one LDS buffer (the next step's tiles wait in
+// registers until every wave is done with the current ones), so four
+// workgroups fit on a CU; the four walks merge in LDS in wave order.
 template <typename T, int D, bool CAUSAL, int SPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
@@ -82,10 +86,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
   using C = FwdTile<T, D>;
   constexpr int CH = C::CH, BC = C::BC, KS = C::KS, VS = C::VS;
   constexpr int BR = 32 * C::NW / SPLIT;  // query rows per workgroup
+  constexpr int NBUF = SPLIT == 4 ? 1 : 2;  // LDS buffers of tiles
   constexpr int CHUNKS = SPLIT * C::CHUNKS;
   constexpr int PER_T = (CHUNKS + 255) / 256;
-  __shared__ __attribute__((aligned(16))) T Ks[2][SPLIT * BC * KS];
-  __shared__ __attribute__((aligned(16))) T Vs[2][SPLIT * BC * VS];
+  __shared__ __attribute__((aligned(16))) T Ks[NBUF][SPLIT * BC * KS];
+  __shared__ __attribute__((aligned(16))) T Vs[NBUF][SPLIT * BC * VS];
+  // Merge area of the four-walk split (three walks' max, sums and
+  // accumulators): the K tiles when they are large enough, else its own.
+  constexpr int XSLOT = C::NB * 16 * 64 + 2 * 64;
+  constexpr int XM = (SPLIT == 4 && 3 * XSLOT * sizeof(float) > sizeof(T) * NBUF * SPLIT * BC * KS) ? 3 * XSLOT : 1;
+  __shared__ __attribute__((aligned(16))) float Xm[XM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -251,17 +261,65 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const T* __restrict__ Q, co
       const bool more = st + 1 < n_st;
       if (more) load_step(st + 1);
       const int kt = SPLIT * st + kp;  // this wave's tile (uniform per wave)
-      const T* ks = &Ks[st & 1][kp * BC * KS];
-      const T* vs = &Vs[st & 1][kp * BC * VS];
+      const T* ks = &Ks[(st & 1) % NBUF][kp * BC * KS];
+      const T* vs = &Vs[(st & 1) % NBUF][kp * BC * VS];
       if (kt < kt_full)
         tile(kt, ks, vs, BoolC<false>{});
       else if (kt < n_kt)
         tile(kt, ks, vs, BoolC<true>{});
-      if (more) store_step((st + 1) & 1);
+      if constexpr (NBUF == 1) {
+        __syncthreads();  // every wave is done with the one buffer
+        if (more) store_step(0);
+      } else {
+        if (more) store_step((st + 1) & 1);
+      }
       __syncthreads();
     }
   }
 
+  if constexpr (SPLIT == 4) {
+    // Merge the four walks: waves 1..3 leave their max, sums and accumulators
+    // in LDS (the last step ended with a barrier), wave 0 (which walked key
+    // 0, so its max is finite) combines them in wave order.
+    constexpr int SLOT = XSLOT;  // floats per walk
+    float* xo = XM > 1 ? Xm : reinterpret_cast<float*>(&Ks[0][0]);
+    if (kp > 0) {
+      float* my = xo + (kp - 1) * SLOT;
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) my[(16 * b + r) * 64 + lane] = o[b][r];
+      my[C::NB * 16 * 64 + lane] = m_run;
+      my[C::NB * 16 * 64 + 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kp > 0) return;
+    float mp[3], lp[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      mp[i] = xo[i * SLOT + C::NB * 16 * 64 + lane];
+      lp[i] = xo[i * SLOT + C::NB * 16 * 64 + 64 + lane];
+    }
+    const float m = fmaxf(fmaxf(m_run, mp[0]), fmaxf(mp[1], mp[2]));
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+    float ap[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) ap[i] = mp[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp[i] - m);
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = o[b][r] * a0;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) x += xo[i * SLOT + (16 * b + r) * 64 + lane] * ap[i];
+        o[b][r] = x;
+      }
+    float l = l_run * a0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) l += lp[i] * ap[i];
+    l_run = l;
+    m_run = m;
+  }
   if constexpr (SPLIT == 2) {
     // Merge the two walks of each query group: the odd wave leaves its max,
     // sums and accumulators in LDS (the tiles are no longer read: the last
@@ -578,11 +636,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   const long long blocks4 = (long long)((a.N + C::BR - 1) / C::BR) * BH;
   if constexpr (sizeof(T) == 4 && D <= 64) {
     // fp32 grids of fewer than two 128-row tiles per CU: split each walk
-    // over two waves (half-size query tiles, so twice the workgroups).
+    // over two waves (half-size query tiles, so twice the workgroups), or at
+    // d <= 32, where four one-buffer workgroups fit on a CU, over four
+    // (quarter-size query tiles).
     if (a.Nk == 0 && blocks4 < kFwdSplitGrid) {
-      const int num_qt = (a.N + C::BR / 2 - 1) / (C::BR / 2);
+      constexpr int SP = D <= 32 ? 4 : 2;
+      const int num_qt = (a.N + C::BR / SP - 1) / (C::BR / SP);
       const long long blocks = (long long)num_qt * BH;
-      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, 2>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, SP>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                          static_cast<T*>(a.o), a.lse, a.N, BH, num_qt, sl2, a.H, a.H / a.Hkv, a.cu, a.T, a.Nk,
                          (int)(blocks <= kFwdSplitGrid));

@@ -244,6 +244,16 @@ def test_gpu_invariants_large_causal():
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
+# 81920 heads of a short sequence: every kernel's grid holds more than 65535
+# workgroups (the head index runs past 16 bits), with the heads' order
+# grouped per XCD as in other grids of 256 or more heads; compared whole.
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", [(512, 160, 9, 32, "bf16", True),
+                                                  (256, 320, 33, 16, "f32", False),
+                                                  (160, 512, 5, 128, "bf16", True)])
+def test_many_heads(B, H, N, d, dtype, causal):
+    run_case(workloads.custom(B, H, N, d, dtype, causal, 3400 + N + d))
+
+
 def test_long_sequence_sampled_rows():
     """N = 65536 (2 heads, d = 128, causal bf16), far past what the oracle
     can materialise: forward rows sampled across the sequence against the

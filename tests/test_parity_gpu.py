@@ -503,12 +503,14 @@ def test_negative_scale(B, H, H_kv, N, d, dtype, causal):
     run_case(w, scale=-1.3 / math.sqrt(d))
 
 
-def test_internal_workspace_on_a_side_stream():
+def test_internal_workspace_on_a_side_stream(monkeypatch):
     """Backward and decoding enqueued on a side stream with no workspace
     passed: the binding allocates the workspace itself and must keep its
     memory for the side stream's kernels while the current stream allocates
     blocks of the same size and fills them.  Results must equal those of
-    the same calls on the current stream, bit for bit."""
+    the same calls on the current stream, bit for bit.  (The tuned kernels:
+    generic decoding needs no workspace.)"""
+    monkeypatch.delenv("FA2_FORCE_GENERIC", raising=False)
     w = workloads.custom(2, 8, 1000, 128, "bf16", True, 8101, name="side", H_kv=2)
     log("case: %s seed=%d" % (w.describe(), w.seed))
     q, k, v, dO = workloads.make_inputs(w, device="cuda")

@@ -503,6 +503,34 @@ def test_negative_scale(B, H, H_kv, N, d, dtype, causal):
     run_case(w, scale=-1.3 / math.sqrt(d))
 
 
+# The autograd bridge: gradients of sum(O * dO) through torch.autograd equal
+# the oracle's dQ, dK, dV (grouped heads included), and a non-contiguous
+# upstream gradient is accepted.
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", [(2, 4, 2, 300, 128, "bf16", True),
+                                                       (1, 3, 3, 130, 64, "f32", False),
+                                                       (1, 2, 1, 77, 32, "f16", True)])
+def test_autograd_attention(B, H, H_kv, N, d, dtype, causal):
+    w = workloads.custom(B, H, N, d, dtype, causal, 3500 + N + d, H_kv=H_kv)
+    log("case: %s seed=%d" % (w.describe(), w.seed))
+    q, k, v, dO = workloads.make_inputs(w, device="cuda")
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention(qa, ka, va, causal)
+    # dO through a transposed copy: the gradient reaching the bridge is
+    # a non-contiguous view with dO's values
+    g = dO.transpose(2, 3).contiguous().transpose(2, 3)
+    assert not g.is_contiguous()
+    o.backward(g)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(q)
+    fa.fa2_forward_ex(q, k, v, o2, lse, causal, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2), "autograd forward differs from fa2_forward_ex"
+    errs = check_against_oracle(w, q, k, v, dO, (o.detach(), lse, qa.grad, ka.grad, va.grad))
+    log("  errors: " + " ".join("%s=%.3g" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
+    assert not bad, bad
+
+
 def test_internal_workspace_on_a_side_stream(monkeypatch):
     """Backward and decoding enqueued on a side stream with no workspace
     passed: the binding allocates the workspace itself and must keep its

@@ -404,7 +404,7 @@ def fa2_decode(q, k, v, o, lse, causal: bool = False, scale: float | None = None
 
 def decode(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
     """Return (o, lse) of q [B, H, N_q, d] against the cache k, v
-    [B, H_kv, N_k, d] (bfloat16 or float16, d = 128)."""
+    [B, H_kv, N_k, d] (float32, bfloat16 or float16; d = 16, 32, 64, 128)."""
     B, H, Nq, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -416,7 +416,7 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, stream=Non
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
     """Return (o, lse) for q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv
-    dividing H) float32 or bfloat16 GPU tensors."""
+    dividing H) float32, bfloat16 or float16 GPU tensors."""
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -435,3 +435,30 @@ def backward(q, k, v, o, lse, dO, causal: bool = True, scale: float | None = Non
         _record(t, stream)
     fa2_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, causal, scale, workspace, stream)
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """torch.autograd bridge: the forward pass runs ``forward`` (keeping o and
+    lse for the backward), the backward pass ``backward``; both on the current
+    stream."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = forward(q, k, v, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, dO.contiguous(), ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal: bool = True, scale: float | None = None):
+    """O = softmax(scale * q k^T + mask) v for contiguous q [B, H, N, d] and
+    k, v [B, H_kv, N, d] on the GPU, differentiable in q, k and v through
+    torch.autograd (the library's forward and backward kernels; scale
+    defaults to 1/sqrt(d))."""
+    return _Attention.apply(q, k, v, causal, scale)

@@ -13,7 +13,8 @@ grouped-query attention, ``fa2_backward_workspace_size`` (``_ex``),
 ``fa2_decode``, ``fa2_decode_workspace_size``, ``fa2_status_string``) take
 caller-allocated tensors like the C ABI; ``forward`` / ``backward`` /
 ``decode`` allocate the outputs (K and V may have fewer heads than Q: H_kv
-dividing H).
+dividing H); ``attention`` is the same forward and backward as a
+``torch.autograd.Function``.
 """
 from __future__ import annotations
 

@@ -25,7 +25,8 @@
  *   - Every pointer must be 16-byte aligned.  Outputs must not alias inputs
  *     or each other.
  *   - The caller owns every buffer (inputs, outputs, workspace).  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls, apart from the
+ *     static per-GPU workspace of fa2_backward_noalloc (below).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work and return; results are valid once the stream
  *     has completed it.  Calls are reentrant and thread-safe.
@@ -101,8 +102,10 @@ size_t fa2_backward_workspace_size(int B, int H, int N, int d, int dtype);
  * of fa2_forward for the same q, k, v, scale and causal.  Overwrites dq, dk,
  * dv (never accumulates into them).  Kernels, in stream order:
  *   1. a query-tile-parallel kernel that computes D_i = sum_k dO_ik O_ik
- *      (fp32) and LSE_i * log2(e) for its rows into the workspace, then
- *      recomputes P and dP and accumulates dQ in registers;
+ *      (fp32; a row whose keys all lie in its first 32-key block takes
+ *      sum_j P_ij dP_ij from that block instead, free of O's rounding) and
+ *      LSE_i * log2(e) for its rows into the workspace, then recomputes P
+ *      and dP and accumulates dQ in registers;
  *   2. a key-tile-parallel kernel that recomputes P from q, k and lse and
  *      accumulates dK and dV in registers.
  * No atomics: every output element is written once by one workgroup, or

@@ -503,6 +503,47 @@ def test_negative_scale(B, H, H_kv, N, d, dtype, causal):
     run_case(w, scale=-1.3 / math.sqrt(d))
 
 
+def test_concurrent_calls_from_two_threads():
+    """The ABI is reentrant: two host threads, each with its own stream,
+    enqueue forward and backward passes of different problems at the same
+    time (ctypes releases the interpreter lock during the calls); every
+    result equals the same call made alone, bit for bit."""
+    import threading
+    cases = [workloads.custom(2, 4, 700, 128, "bf16", True, 3601, H_kv=2),
+             workloads.custom(2, 4, 513, 64, "f32", False, 3602)]
+    inputs = [workloads.make_inputs(w, device="cuda") for w in cases]
+
+    def run(w, q, k, v, dO, stream):
+        with torch.cuda.stream(stream):
+            o, lse = fa.forward(q, k, v, w.causal, w.scale, stream=stream)
+            return (o, lse) + fa.backward(q, k, v, o, lse, dO, w.causal, w.scale, stream=stream)
+
+    ref = [run(w, *x, torch.cuda.current_stream()) for w, x in zip(cases, inputs)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    out = [[None] * 4 for _ in cases]
+    errors = []
+
+    def worker(i):
+        try:
+            for r in range(4):
+                out[i][r] = run(cases[i], *inputs[i], streams[i])
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for r in range(4):
+            for a, b, name in zip(out[i][r], ref[i], ("O", "LSE", "dQ", "dK", "dV")):
+                assert torch.equal(a, b), "case %d round %d: %s differs" % (i, r, name)
+
+
 # The autograd bridge: gradients of sum(O * dO) through torch.autograd equal
 # the oracle's dQ, dK, dV (grouped heads included), and a non-contiguous
 # upstream gradient is accepted.
